@@ -1,0 +1,43 @@
+"""fp64 CPU oracle for decode-context-parallel (DCP) attention.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+path (``kv_cache_context_amd``) never imports it, and it never imports the
+product path.  It shares no code with the HIP kernels; the only thing both
+sides read is the seeded input generator in ``workloads``.
+
+Every function follows a stated definition:
+
+* ``softmax_attention`` — plain softmax attention of one decode query per head
+  against a set of keys/values, returning the normalized output and the
+  natural-log log-sum-exp of the scaled scores.  This is what each rank
+  computes over its local slice in the "Compute" step of the DCP process
+  (vLLM blog post on Decode Context Parallelism, section 4.1).
+* ``mla_attention`` — the MLA form in absorbed latent space: keys are the
+  full latent row [c_kv | k_rope] (576 wide), values are c_kv (512 wide); one
+  latent row serves every query head (same post, section 5.3 "MLA Backend").
+* ``gqa_attention`` — each KV head serves a consecutive group of query heads
+  (section 5.4 "GQA Backend").
+* ``shard_positions`` — which global token positions a shard holds
+  (section 4; round-robin and contiguous layouts).
+* ``merge`` — the LSE-weighted merge of N partial results into the exact
+  output (section 4.1, the AllGather + ReduceScatter step, which reweights
+  partial outputs by their LSE values).
+* ``bf16_rne`` — round-to-nearest-even cast of fp32 to bf16 (the output cast).
+
+Parity of every function here is pinned by the CPU tests in
+``tests/test_oracle_pins.py`` against closed forms, library routines and
+invariants; see the notes there.
+"""
+from .attention import (  # noqa: F401
+    widen_bf16,
+    softmax_attention,
+    mla_attention,
+    gqa_attention,
+    shard_positions,
+    mla_shard_partial,
+    gqa_shard_partial,
+    merge,
+    bf16_rne,
+    bf16_rne_bits,
+)

@@ -1,0 +1,93 @@
+"""Seeded input generator: determinism, paged layout, length statistics."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as O
+
+
+def test_bf16_bits_match_torch():
+    r = np.random.default_rng(1)
+    x = r.standard_normal(100000).astype(np.float32) * 3
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(W.f32_to_bf16_bits(x), ref)
+    assert np.array_equal(W.bf16_bits_to_f32(ref).astype(np.float64), O.widen_bf16(ref))
+
+
+def test_generation_is_deterministic_and_chunk_independent():
+    w = W.custom_workload(batch=2, heads=4, seq_lens=(W.CHUNK + 77, 5), num_shards=3)
+    a = W.Case(w, seed=3)
+    b = W.Case(w, seed=3)
+    assert np.array_equal(a.q, b.q)
+    full = a.kv_logical(0)
+    assert full.shape == (W.CHUNK + 77, 576)
+    assert np.array_equal(full[W.CHUNK - 5: W.CHUNK + 9], b.kv_logical(0, W.CHUNK - 5, W.CHUNK + 9))
+    pos = [W.CHUNK + 3, 2, W.CHUNK - 1, 0]
+    assert np.array_equal(a.rows_at(0, pos)[0], full[pos])
+    assert not np.array_equal(W.Case(w, seed=4).q, a.q)
+
+
+@pytest.mark.parametrize("layout", [W.ROUND_ROBIN, W.CONTIGUOUS])
+@pytest.mark.parametrize("kind", ["mla", "gqa"])
+def test_pool_gathers_back_to_oracle_slices(layout, kind):
+    """Reading each shard's pool through its table gives exactly the tokens the
+    oracle assigns to that shard, in order."""
+    lens = (1, 3, 17, 64, 65, 200)
+    n = 4
+    if kind == "mla":
+        w = W.custom_workload(kind="mla", batch=len(lens), heads=2, seq_lens=lens, num_shards=n,
+                              layout=layout, block_size=16)
+    else:
+        w = W.custom_workload(kind="gqa", batch=len(lens), heads=8, kv_heads=2, head_dim=16,
+                              seq_lens=lens, num_shards=n, layout=layout, block_size=16)
+    case = W.Case(w, seed=0)
+    seen_blocks = []
+    for r in range(n):
+        sc = case.shard(r)
+        used = []
+        for b, L in enumerate(lens):
+            idx = O.shard_positions(L, n, r, layout)
+            assert sc.local_lens[b] == len(idx)
+            j = np.arange(len(idx))
+            blk = sc.block_table[b, j // w.block_size]
+            used.extend(sorted(set(blk.tolist())))
+            logical = case.kv_logical(b)
+            logical = (logical,) if kind == "mla" else logical
+            for pool, ref in zip(sc.pools, logical):
+                assert np.array_equal(pool[blk, j % w.block_size], ref[idx])
+        # block ids of one shard are a permutation of its pool
+        assert sorted(used) == list(range(len(used))) or len(used) == 0
+        seen_blocks.append(len(used))
+
+
+def test_block_table_is_shuffled():
+    case = W.Case(W.WORKLOADS["c0"])
+    t, nb = case.block_table(1)
+    assert nb == 2 * 4 and sorted(t[:, :4].ravel().tolist()) == list(range(8))
+    assert t[:, :4].ravel().tolist() != list(range(8))
+
+
+def test_bimodal_sampler_statistics():
+    L = W.sample_bimodal_lengths(20000, np.random.default_rng(0))
+    k = 1024
+    assert 0.16 < np.mean(L < 8 * k) < 0.20
+    assert 0.45 < np.mean(L < 64 * k) < 0.49
+    assert 62 * k < np.median(L) < 72 * k
+    assert 0.02 < np.mean(L > 256 * k) < 0.05
+    assert L.max() <= 512 * k and L.min() >= k
+
+
+def test_c2_lengths_fixed_by_seed():
+    a = W.Case(W.WORKLOADS["c2"], seed=0).seq_lens
+    assert a.shape == (32,) and np.array_equal(a, W.Case(W.WORKLOADS["c2"], seed=0).seq_lens)
+
+
+def test_workload_shapes():
+    w = W.WORKLOADS
+    assert (w["c1"].heads, w["c1"].dk, w["c1"].dv, w["c1"].num_shards) == (64, 576, 512, 8)
+    assert abs(w["c0"].scale - 192 ** -0.5) < 1e-15 and abs(w["c3"].scale - 128 ** -0.5) < 1e-15
+    c3 = W.Case(w["c3"])
+    assert c3.max_blocks_per_seq() == 2048 and c3.local_lens(1)[0] == 32768
+    c4b = W.Case(w["c4b"])
+    assert c4b.local_lens(1).sum() == 128 * 8192
