@@ -1,0 +1,239 @@
+// Host side of the C ABI: argument validation, launch planning, status codes.
+// Nothing here reads device memory or synchronizes; every launch goes to the
+// caller's stream.
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "dcp.h"
+#include "dcp_internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+dcp_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return DCP_OK;
+  g_last_hip_error = (int)e;
+  return DCP_ERR_HIP;
+}
+
+int env_int(const char* name, int dflt, int lo, int hi) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  long x = std::strtol(v, nullptr, 10);
+  if (x < lo) x = lo;
+  if (x > hi) x = hi;
+  return (int)x;
+}
+
+// Compute units of the current device, cached per device.
+int device_cus(hipError_t* err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { *err = e; return 0; }
+  static std::atomic<int> cache[64];
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || cus <= 0) { *err = e != hipSuccess ? e : hipErrorInvalidDevice; return 0; }
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Checks shared by both partial entry points.
+dcp_status check_split(int batch, int block_size, int max_blocks, int num_blocks, int rank,
+                       int nshards, dcp_layout layout, int hint, float scale) {
+  if (batch < 0 || nshards < 1 || rank < 0 || rank >= nshards) return DCP_ERR_INVALID_ARGUMENT;
+  if (layout != DCP_LAYOUT_ROUND_ROBIN && layout != DCP_LAYOUT_CONTIGUOUS) return DCP_ERR_INVALID_ARGUMENT;
+  if (block_size < 1 || max_blocks < 1 || num_blocks < 1 || hint < 1) return DCP_ERR_INVALID_ARGUMENT;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return DCP_ERR_INVALID_ARGUMENT;
+  if (block_size % 16 != 0 || block_size > 1024) return DCP_ERR_UNSUPPORTED;
+  const int64_t cap = (int64_t)max_blocks * block_size;
+  if (cap > INT32_MAX) return DCP_ERR_UNSUPPORTED;
+  // the longest local slice of a request of length `hint` must fit one table row
+  const int64_t local_max = ((int64_t)hint + nshards - 1) / nshards;
+  if (local_max > cap) return DCP_ERR_INVALID_ARGUMENT;
+  if (batch > dcp::kMaxBatch) return DCP_ERR_UNSUPPORTED;
+  return DCP_OK;
+}
+
+dcp::SplitArgs split_args(int batch, int block_size, int max_blocks, int num_blocks, int rank,
+                          int nshards, dcp_layout layout, float scale, const int32_t* table,
+                          const int32_t* seq_lens, float* out, float* lse, void* ws,
+                          const dcp::WsLayout& wl) {
+  dcp::SplitArgs s;
+  s.table = table;
+  s.seq_lens = seq_lens;
+  s.ws_meta = (int32_t*)((char*)ws + wl.meta_off);
+  s.ws_ml = (float*)((char*)ws + wl.ml_off);
+  s.ws_o = (float*)((char*)ws + wl.o_off);
+  s.out = out;
+  s.lse = lse;
+  s.batch = batch;
+  s.block_size = block_size;
+  s.max_blocks = max_blocks;
+  s.num_blocks = num_blocks;
+  s.rank = rank;
+  s.nshards = nshards;
+  s.layout = (int)layout;
+  s.G = 0;
+  s.min_tiles = 1;
+  s.scale = scale;
+  s.c = scale * 1.4426950408889634f;
+  return s;
+}
+
+dcp_status mla_check(const dcp_mla_params* p) {
+  if (!p) return DCP_ERR_INVALID_ARGUMENT;
+  if (p->num_heads < 1 || p->kv_lora_rank < 1 || p->rope_dim < 1) return DCP_ERR_INVALID_ARGUMENT;
+  dcp_status st = check_split(p->batch, p->block_size, p->max_blocks_per_seq, p->num_blocks,
+                              p->shard_rank, p->num_shards, p->layout, p->max_seq_len_hint,
+                              p->softmax_scale);
+  if (st != DCP_OK) return st;
+  if (p->kv_lora_rank != 512 || p->rope_dim != 64) return DCP_ERR_UNSUPPORTED;
+  if (p->num_heads % 16 != 0 || p->num_heads > 64) return DCP_ERR_UNSUPPORTED;
+  return DCP_OK;
+}
+
+dcp_status gqa_check(const dcp_gqa_params* p) {
+  if (!p) return DCP_ERR_INVALID_ARGUMENT;
+  if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1) return DCP_ERR_INVALID_ARGUMENT;
+  if (p->num_q_heads % p->num_kv_heads != 0) return DCP_ERR_INVALID_ARGUMENT;
+  dcp_status st = check_split(p->batch, p->block_size, p->max_blocks_per_seq, p->num_blocks,
+                              p->shard_rank, p->num_shards, p->layout, p->max_seq_len_hint,
+                              p->softmax_scale);
+  if (st != DCP_OK) return st;
+  if (p->head_dim != 128) return DCP_ERR_UNSUPPORTED;
+  if (p->num_kv_heads % 4 != 0 || p->num_kv_heads > 64) return DCP_ERR_UNSUPPORTED;
+  if (p->num_q_heads / p->num_kv_heads > 16) return DCP_ERR_UNSUPPORTED;
+  return DCP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dcp_abi_version(void) { return DCP_ABI_VERSION; }
+
+int dcp_last_hip_error(void) { return g_last_hip_error; }
+
+const char* dcp_status_string(dcp_status s) {
+  switch (s) {
+    case DCP_OK: return "ok";
+    case DCP_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DCP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DCP_ERR_WORKSPACE: return "workspace missing or too small";
+    case DCP_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+size_t dcp_mla_workspace_bytes(const dcp_mla_params* p) {
+  if (mla_check(p) != DCP_OK) return 0;
+  return dcp::ws_layout(p->batch, p->num_heads, 512).total;
+}
+
+dcp_status dcp_mla_decode_partial(const dcp_mla_params* p, const void* q, const void* kv_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens, float* out,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  dcp_status st = mla_check(p);
+  if (st != DCP_OK) return st;
+  if (p->batch == 0) return DCP_OK;
+  if (!q || !kv_cache || !block_table || !seq_lens || !out || !lse) return DCP_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4) || !aligned(lse, 4))
+    return DCP_ERR_INVALID_ARGUMENT;
+  const dcp::WsLayout wl = dcp::ws_layout(p->batch, p->num_heads, 512);
+  if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
+  hipError_t herr = hipSuccess;
+  const int cus = device_cus(&herr);
+  if (cus <= 0) return hip_status(herr);
+
+  dcp::MlaArgs a;
+  a.s = split_args(p->batch, p->block_size, p->max_blocks_per_seq, p->num_blocks, p->shard_rank,
+                   p->num_shards, p->layout, p->softmax_scale, block_table, seq_lens, out, lse,
+                   workspace, wl);
+  a.s.G = env_int("DCP_SPLIT_WGS", cus < dcp::kMaxSplitWGs ? cus : dcp::kMaxSplitWGs, 1,
+                  dcp::kMaxSplitWGs);
+  a.s.min_tiles = env_int("DCP_MLA_MIN_TILES", 8, 1, 1 << 20);
+  a.q = (const uint16_t*)q;
+  a.kv = (const uint16_t*)kv_cache;
+  a.heads = p->num_heads;
+  return hip_status(dcp::launch_mla_partial(a, stream));
+}
+
+size_t dcp_gqa_workspace_bytes(const dcp_gqa_params* p) {
+  if (gqa_check(p) != DCP_OK) return 0;
+  return dcp::ws_layout(p->batch, p->num_q_heads, 128).total;
+}
+
+dcp_status dcp_gqa_decode_partial(const dcp_gqa_params* p, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, float* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  dcp_status st = gqa_check(p);
+  if (st != DCP_OK) return st;
+  if (p->batch == 0) return DCP_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !lse)
+    return DCP_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(lse, 4))
+    return DCP_ERR_INVALID_ARGUMENT;
+  const dcp::WsLayout wl = dcp::ws_layout(p->batch, p->num_q_heads, 128);
+  if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
+  hipError_t herr = hipSuccess;
+  const int cus = device_cus(&herr);
+  if (cus <= 0) return hip_status(herr);
+
+  dcp::GqaArgs a;
+  a.s = split_args(p->batch, p->block_size, p->max_blocks_per_seq, p->num_blocks, p->shard_rank,
+                   p->num_shards, p->layout, p->softmax_scale, block_table, seq_lens, out, lse,
+                   workspace, wl);
+  // one workgroup column per group of 4 KV heads; together they fill the chip once
+  const int groups = p->num_kv_heads / 4;
+  int g = (cus + groups - 1) / groups;
+  if (g > dcp::kMaxSplitWGs) g = dcp::kMaxSplitWGs;
+  a.s.G = env_int("DCP_SPLIT_WGS", g, 1, dcp::kMaxSplitWGs);
+  a.s.min_tiles = env_int("DCP_GQA_MIN_TILES", 16, 1, 1 << 20);
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k_cache;
+  a.v = (const uint16_t*)v_cache;
+  a.hq = p->num_q_heads;
+  a.hkv = p->num_kv_heads;
+  return hip_status(dcp::launch_gqa_partial(a, stream));
+}
+
+dcp_status dcp_combine(int32_t num_shards, int32_t batch, int32_t num_heads, int32_t head_dim_v,
+                       const float* partial_out, const float* partial_lse, void* out_bf16,
+                       float* out_f32, float* lse_out, hipStream_t stream) {
+  if (num_shards < 1 || batch < 0 || num_heads < 1 || head_dim_v < 1) return DCP_ERR_INVALID_ARGUMENT;
+  if (num_shards > 64 || head_dim_v % 4 != 0 || head_dim_v > 1024) return DCP_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)batch * num_heads;
+  if (rows > INT32_MAX / 4) return DCP_ERR_UNSUPPORTED;
+  if (rows == 0) return DCP_OK;
+  if (!partial_out || !partial_lse || (!out_bf16 && !out_f32)) return DCP_ERR_INVALID_ARGUMENT;
+  if (!aligned(partial_out, 16) || !aligned(partial_lse, 4) || !aligned(out_bf16, 8) ||
+      !aligned(out_f32, 16) || !aligned(lse_out, 4))
+    return DCP_ERR_INVALID_ARGUMENT;
+  dcp::CombineArgs a;
+  a.po = partial_out;
+  a.plse = partial_lse;
+  a.out_bf16 = (uint16_t*)out_bf16;
+  a.out_f32 = out_f32;
+  a.lse_out = lse_out;
+  a.nshards = num_shards;
+  a.rows = (int)rows;
+  a.dv = head_dim_v;
+  a.pad = 0.f;
+  return hip_status(dcp::launch_combine(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,125 @@
+// Device-side helpers shared by the DCP kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dcp {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;  // one 16x16x32 MFMA operand
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+
+#define DCP_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// D[16x16] += A[16x32] * B[32x16], bf16 inputs, fp32 accumulate.
+// Lane l holds A row l%16 / B column l%16, k-slots 8*(l/16)..+7; D column l%16,
+// rows 4*(l/16)..+3.
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D[16x16] += A[16x16] * B[16x16]; lane l holds k-slots 4*(l/16)..+3.
+__device__ __forceinline__ f32x4 mfma_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read: inside each group of 16 lanes, lane i receives element
+// (i % 4) of the 4 x 16-bit values loaded by lanes 4*j + i/4, j = 0..3.  With
+// lane L of a group pointing at row (L/4), columns 4*(L%4)..+3 of a row-major
+// 4 x 16 tile, lane i gets column i of the 4 rows.
+__device__ __forceinline__ i16x4 lds_read_tr16(const DCP_LDS char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((DCP_LDS i16x4*)p);
+}
+
+// Mark a value as uniform across the wave (keeps it, and loads addressed by it, scalar).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Read-only load through the scalar cache (index must be wave-uniform).  Used
+// for block-table entries and lengths, which the kernels never write.
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Copy 16 bytes global -> LDS without passing through registers
+// (global_load_lds_dwordx4).  `lds_wave_base` must be the same for all lanes of
+// the wave; lane i writes base + 16*i.  Issued from inline assembly on purpose:
+// the compiler then does not add its own conservative "wait for every LDS copy"
+// before later LDS reads.  The caller owns completion: wait_vmcnt<N>() (vector
+// memory operations of a wave complete in issue order) followed by barrier().
+__device__ __forceinline__ void dma16(const void* src, DCP_LDS void* lds_wave_base) {
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)lds_wave_base);
+  // m0 is reserved: the compiler keeps no value in it across statements here
+  // (it sets m0 itself right before each of its own uses).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(m0)
+      : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0) only
+
+// Workgroup barrier that neither waits on memory counters nor lets the compiler
+// move memory accesses across it.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ float wave_max16(float v) {  // over lanes l, l^16, l^32, l^48
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum16(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Number of a request's L global tokens that live on shard r of n.
+// Round-robin: positions r, r+n, ...; contiguous: [r*C, min(L,(r+1)*C)), C = ceil(L/n).
+__device__ __forceinline__ int local_len(int L, int n, int r, int layout) {
+  if (L <= 0) return 0;
+  const int64_t LL = L;
+  if (layout == 0) return LL > r ? (int)((LL - r + n - 1) / n) : 0;
+  const int64_t c = (LL + n - 1) / n;
+  const int64_t lo = c * r;
+  const int64_t hi = LL < lo + c ? LL : lo + c;
+  return hi > lo ? (int)(hi - lo) : 0;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  __bf16 x = (__bf16)a, y = (__bf16)b;  // round to nearest even (v_cvt_pk_bf16_f32)
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+}  // namespace dcp

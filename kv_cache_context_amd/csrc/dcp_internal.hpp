@@ -1,0 +1,79 @@
+// Internal (non-ABI) declarations shared by the host layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dcp {
+
+// Upper bound on the number of split workgroups one partial call launches.  The
+// workspace is sized for it, so its size depends on (batch, heads) only.
+constexpr int kMaxSplitWGs = 512;
+// Largest batch the in-kernel split planner handles (its prefix sums sit in LDS).
+constexpr int kMaxBatch = 2048;
+
+// Workspace layout of a partial call (all offsets 256-byte aligned):
+//   meta  int32 [kMaxBatch + 2]: [0] = split WGs used, [1 + b] = tile prefix sum
+//   ml    fp32  [slots][heads][2]: running max (raw score units) and softmax sum
+//   o     fp32  [slots][heads][dv]: unnormalized partial output
+// slots = kMaxSplitWGs + batch.
+struct WsLayout {
+  size_t meta_off, ml_off, o_off, total;
+};
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline WsLayout ws_layout(int batch, int heads, int dv) {
+  WsLayout w;
+  const size_t slots = (size_t)kMaxSplitWGs + (size_t)batch;
+  w.meta_off = 0;
+  w.ml_off = align256(sizeof(int32_t) * (kMaxBatch + 2));
+  w.o_off = w.ml_off + align256(sizeof(float) * slots * heads * 2);
+  w.total = w.o_off + align256(sizeof(float) * slots * heads * dv);
+  return w;
+}
+
+struct SplitArgs {
+  const int32_t* table;
+  const int32_t* seq_lens;
+  int32_t* ws_meta;
+  float* ws_ml;
+  float* ws_o;
+  float* out;
+  float* lse;
+  int batch, block_size, max_blocks, num_blocks, rank, nshards, layout;
+  int G;          // split workgroups launched
+  int min_tiles;  // fewest tiles a split workgroup is given
+  float scale;    // softmax scale
+  float c;        // softmax scale * log2(e)
+};
+
+struct MlaArgs {
+  SplitArgs s;
+  const uint16_t* q;
+  const uint16_t* kv;
+  int heads;
+};
+
+struct GqaArgs {
+  SplitArgs s;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int hq, hkv;
+};
+
+struct CombineArgs {
+  const float* po;
+  const float* plse;
+  uint16_t* out_bf16;
+  float* out_f32;
+  float* lse_out;
+  int nshards, rows, dv;
+  float pad;
+};
+
+hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_gqa_partial(const GqaArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace dcp

@@ -1,0 +1,130 @@
+"""Tensor-level wrappers over the C ABI (argument checking and marshalling only).
+
+Each function validates shapes, dtypes, devices and contiguity of torch
+tensors, fills the parameter struct and calls the library entry point of the
+same name on the given stream.  No arithmetic of the method happens here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import dcp as _abi
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _req(t: torch.Tensor, dtype, ndim: int, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def mla_params(*, batch, num_heads, block_size, max_blocks_per_seq, num_blocks, shard_rank, num_shards,
+               layout, max_seq_len_hint, softmax_scale, kv_lora_rank=512, rope_dim=64) -> _abi.dcp_mla_params:
+    return _abi.dcp_mla_params(batch, num_heads, kv_lora_rank, rope_dim, block_size, max_blocks_per_seq,
+                               num_blocks, shard_rank, num_shards, layout, max_seq_len_hint, softmax_scale)
+
+
+def gqa_params(*, batch, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, num_blocks, shard_rank,
+               num_shards, layout, max_seq_len_hint, softmax_scale, head_dim=128) -> _abi.dcp_gqa_params:
+    return _abi.dcp_gqa_params(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                               num_blocks, shard_rank, num_shards, layout, max_seq_len_hint, softmax_scale)
+
+
+def mla_workspace(p: _abi.dcp_mla_params, device) -> torch.Tensor:
+    n = _abi.dcp_mla_workspace_bytes(p)
+    if n == 0:
+        raise _abi.DcpError(_abi.DCP_ERR_INVALID_ARGUMENT, "dcp_mla_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def gqa_workspace(p: _abi.dcp_gqa_params, device) -> torch.Tensor:
+    n = _abi.dcp_gqa_workspace_bytes(p)
+    if n == 0:
+        raise _abi.DcpError(_abi.DCP_ERR_INVALID_ARGUMENT, "dcp_gqa_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def dcp_mla_decode_partial(p, q, kv_cache, block_table, seq_lens, out, lse, workspace, stream=None) -> None:
+    _req(q, torch.bfloat16, 3, "q")
+    _req(kv_cache, torch.bfloat16, 3, "kv_cache")
+    _req(block_table, torch.int32, 2, "block_table")
+    _req(seq_lens, torch.int32, 1, "seq_lens")
+    _req(out, torch.float32, 3, "out")
+    _req(lse, torch.float32, 2, "lse")
+    dk = p.kv_lora_rank + p.rope_dim
+    if tuple(q.shape) != (p.batch, p.num_heads, dk):
+        raise ValueError(f"q shape {tuple(q.shape)} != {(p.batch, p.num_heads, dk)}")
+    if tuple(kv_cache.shape) != (p.num_blocks, p.block_size, dk):
+        raise ValueError(f"kv_cache shape {tuple(kv_cache.shape)} != {(p.num_blocks, p.block_size, dk)}")
+    if tuple(block_table.shape) != (p.batch, p.max_blocks_per_seq):
+        raise ValueError(f"block_table shape {tuple(block_table.shape)}")
+    if tuple(seq_lens.shape) != (p.batch,):
+        raise ValueError("seq_lens shape")
+    if tuple(out.shape) != (p.batch, p.num_heads, p.kv_lora_rank) or tuple(lse.shape) != (p.batch, p.num_heads):
+        raise ValueError("out/lse shape")
+    _abi.check(_abi.dcp_mla_decode_partial(p, q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
+                                           seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                           _stream(stream)), "dcp_mla_decode_partial")
+
+
+def dcp_gqa_decode_partial(p, q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace,
+                           stream=None) -> None:
+    _req(q, torch.bfloat16, 3, "q")
+    _req(k_cache, torch.bfloat16, 4, "k_cache")
+    _req(v_cache, torch.bfloat16, 4, "v_cache")
+    _req(block_table, torch.int32, 2, "block_table")
+    _req(seq_lens, torch.int32, 1, "seq_lens")
+    _req(out, torch.float32, 3, "out")
+    _req(lse, torch.float32, 2, "lse")
+    if tuple(q.shape) != (p.batch, p.num_q_heads, p.head_dim):
+        raise ValueError("q shape")
+    kshape = (p.num_blocks, p.block_size, p.num_kv_heads, p.head_dim)
+    if tuple(k_cache.shape) != kshape or tuple(v_cache.shape) != kshape:
+        raise ValueError(f"k/v cache shape must be {kshape}")
+    if tuple(block_table.shape) != (p.batch, p.max_blocks_per_seq) or tuple(seq_lens.shape) != (p.batch,):
+        raise ValueError("block_table / seq_lens shape")
+    if tuple(out.shape) != (p.batch, p.num_q_heads, p.head_dim) or tuple(lse.shape) != (p.batch, p.num_q_heads):
+        raise ValueError("out/lse shape")
+    _abi.check(_abi.dcp_gqa_decode_partial(p, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                           block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                                           lse.data_ptr(), workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(), _stream(stream)),
+               "dcp_gqa_decode_partial")
+
+
+def dcp_combine(partial_out, partial_lse, out_bf16=None, out_f32=None, lse_out=None, stream=None) -> None:
+    _req(partial_out, torch.float32, 4, "partial_out")
+    _req(partial_lse, torch.float32, 3, "partial_lse")
+    n, b, h, dv = partial_out.shape
+    if tuple(partial_lse.shape) != (n, b, h):
+        raise ValueError("partial_lse shape")
+    if out_bf16 is not None:
+        _req(out_bf16, torch.bfloat16, 3, "out_bf16")
+        if tuple(out_bf16.shape) != (b, h, dv):
+            raise ValueError("out_bf16 shape")
+    if out_f32 is not None:
+        _req(out_f32, torch.float32, 3, "out_f32")
+        if tuple(out_f32.shape) != (b, h, dv):
+            raise ValueError("out_f32 shape")
+    if lse_out is not None:
+        _req(lse_out, torch.float32, 2, "lse_out")
+        if tuple(lse_out.shape) != (b, h):
+            raise ValueError("lse_out shape")
+    ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+    _abi.check(_abi.dcp_combine(n, b, h, dv, partial_out.data_ptr(), partial_lse.data_ptr(), ptr(out_bf16),
+                                ptr(out_f32), ptr(lse_out), _stream(stream)), "dcp_combine")

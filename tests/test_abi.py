@@ -1,0 +1,115 @@
+"""The C-ABI library loads on the CPU, exports every declared symbol, and
+rejects bad arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_context_amd import dcp, ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "dcp.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dcp_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = dcp.lib()
+    names = declared_functions()
+    assert set(names) == set(dcp.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert dcp.dcp_abi_version() == 1
+
+
+def test_struct_layout_matches_header():
+    # 11 int32 fields + 1 float, no padding
+    assert ctypes.sizeof(dcp.dcp_mla_params) == 48
+    assert ctypes.sizeof(dcp.dcp_gqa_params) == 48
+
+
+def test_status_strings():
+    assert dcp.status_string(0) == "ok"
+    assert "workspace" in dcp.status_string(3)
+    assert dcp.status_string(99) == "unknown status"
+
+
+def mla(**kw):
+    base = dict(batch=2, num_heads=64, block_size=64, max_blocks_per_seq=16, num_blocks=64, shard_rank=1,
+                num_shards=8, layout=0, max_seq_len_hint=8192, softmax_scale=0.072)
+    base.update(kw)
+    return ops.mla_params(**base)
+
+
+def gqa(**kw):
+    base = dict(batch=2, num_q_heads=64, num_kv_heads=8, block_size=16, max_blocks_per_seq=64, num_blocks=200,
+                shard_rank=1, num_shards=4, layout=0, max_seq_len_hint=4096, softmax_scale=0.088)
+    base.update(kw)
+    return ops.gqa_params(**base)
+
+
+FAKE = 1 << 20  # an aligned non-null address; never dereferenced (validation fails first)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), 1), (dict(num_shards=0), 1), (dict(shard_rank=8), 1), (dict(shard_rank=-1), 1),
+    (dict(layout=7), 1), (dict(block_size=0), 1), (dict(num_blocks=0), 1), (dict(max_seq_len_hint=0), 1),
+    (dict(softmax_scale=0.0), 1), (dict(softmax_scale=float("inf")), 1), (dict(softmax_scale=float("nan")), 1),
+    (dict(num_heads=0), 1), (dict(max_seq_len_hint=8 * 16 * 64 + 1), 1),
+    (dict(num_heads=17), 2), (dict(num_heads=128), 2), (dict(block_size=8), 2), (dict(block_size=2048), 2),
+    (dict(kv_lora_rank=256), 2), (dict(rope_dim=32), 2), (dict(batch=4096), 2),
+])
+def test_mla_validation(kw, status):
+    p = mla(**kw)
+    assert dcp.dcp_mla_decode_partial(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, 0) == status
+    assert dcp.dcp_mla_workspace_bytes(p) == 0
+
+
+def test_mla_pointer_and_workspace_checks():
+    p = mla()
+    need = dcp.dcp_mla_workspace_bytes(p)
+    assert need > 0
+    assert dcp.dcp_mla_decode_partial(p, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, 0) == 1
+    assert dcp.dcp_mla_decode_partial(p, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, 0) == 1
+    assert dcp.dcp_mla_decode_partial(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 0) == 3
+    assert dcp.dcp_mla_decode_partial(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, need, 0) == 3
+    assert dcp.dcp_mla_decode_partial(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, need, 0) == 3
+    # batch 0 is a no-op even with null pointers
+    assert dcp.dcp_mla_decode_partial(mla(batch=0), 0, 0, 0, 0, 0, 0, 0, 0, 0) == 0
+    # workspace grows with batch and heads only
+    assert dcp.dcp_mla_workspace_bytes(mla(batch=4)) > need
+    assert dcp.dcp_mla_workspace_bytes(mla(max_seq_len_hint=100)) == need
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=60), 1), (dict(num_kv_heads=0), 1), (dict(shard_rank=4), 1), (dict(batch=-3), 1),
+    (dict(head_dim=64), 2), (dict(num_kv_heads=2, num_q_heads=16), 2), (dict(num_q_heads=256, num_kv_heads=8), 2),
+    (dict(block_size=24), 2), (dict(max_seq_len_hint=4 * 64 * 16 + 1), 1),
+])
+def test_gqa_validation(kw, status):
+    p = gqa(**kw)
+    assert dcp.dcp_gqa_decode_partial(p, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, 0) == status
+
+
+def test_combine_validation():
+    c = dcp.dcp_combine
+    assert c(0, 1, 1, 512, FAKE, FAKE, FAKE, 0, 0, 0) == 1
+    assert c(65, 1, 1, 512, FAKE, FAKE, FAKE, 0, 0, 0) == 2
+    assert c(8, 1, 1, 510, FAKE, FAKE, FAKE, 0, 0, 0) == 2
+    assert c(8, 1, 1, 2048, FAKE, FAKE, FAKE, 0, 0, 0) == 2
+    assert c(8, 1, 1, 512, FAKE, FAKE, 0, 0, 0, 0) == 1          # no output at all
+    assert c(8, 1, 1, 512, 0, FAKE, FAKE, 0, 0, 0) == 1
+    assert c(8, 1, 1, 512, FAKE + 4, FAKE, FAKE, 0, 0, 0) == 1   # misaligned partials
+    assert c(8, 0, 64, 512, 0, 0, 0, 0, 0, 0) == 0               # empty batch: no-op
+
+
+def test_ops_reject_cpu_tensors():
+    import torch
+    p = mla(batch=1)
+    t = torch.zeros((1, 64, 576), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ops.dcp_mla_decode_partial(p, t, t, t, t, t, t, t)

@@ -212,9 +212,15 @@ class ShardCache:
 class Case:
     """A seeded instance of a workload."""
 
-    def __init__(self, w: Workload, seed: int = 0):
+    def __init__(self, w: Workload, seed: int = 0, q_scale_pow2: int = 0, needles=()):
+        """``q_scale_pow2`` multiplies every query by 2**k (exact in bf16), which
+        sharpens the softmax.  ``needles`` is a list of (request, position,
+        head): the K/V row at that global position is replaced by that head's
+        query, planting one dominant key (MLA only)."""
         self.w = w
         self.seed = seed
+        self.q_scale_pow2 = int(q_scale_pow2)
+        self.needles = tuple(needles)
         if w.seq_lens is None:
             rng = np.random.default_rng([seed, w.wid, T_LEN])
             self.seq_lens = sample_bimodal_lengths(w.batch, rng).astype(np.int32)
@@ -228,8 +234,13 @@ class Case:
     def q(self) -> np.ndarray:
         if self._q is None:
             w = self.w
-            self._q = np.stack([normal_bf16((self.seed, w.wid, T_Q, b, 0), (w.heads, w.dk))
-                                for b in range(w.batch)]) if w.batch else np.zeros((0, w.heads, w.dk), np.uint16)
+            q = np.stack([normal_bf16((self.seed, w.wid, T_Q, b, 0), (w.heads, w.dk))
+                          for b in range(w.batch)]) if w.batch else np.zeros((0, w.heads, w.dk), np.uint16)
+            if self.q_scale_pow2:
+                # add k to the bf16 exponent field (values stay normal for N(0,1) draws)
+                nz = (q & 0x7F80) != 0
+                q = np.where(nz, q + np.uint16((self.q_scale_pow2 & 0xFF) << 7), q).astype(np.uint16)
+            self._q = q
         return self._q
 
     @property
@@ -253,7 +264,11 @@ class Case:
     def _chunk(self, tid: int, b: int, c: int, L: int) -> np.ndarray:
         t0 = c * CHUNK
         n = min(CHUNK, L - t0)
-        return normal_bf16((self.seed, self.w.wid, tid, b, c), (n,) + self._row_shape())
+        a = normal_bf16((self.seed, self.w.wid, tid, b, c), (n,) + self._row_shape())
+        for nb, pos, head in self.needles:
+            if nb == b and t0 <= pos < t0 + n:
+                a[pos - t0] = self.q[b, head]
+        return a
 
     def kv_logical(self, b: int, t0: int = 0, t1: int | None = None):
         """bf16 bits of request b's tokens [t0, t1) in global order.
