@@ -1,0 +1,302 @@
+"""Benchmark of the DCP decode hot path on one MI355X.
+
+A step is one decode step of one attention layer on the timed shard(s): the
+shard-local partial attention (MLA or GQA) over the shard's paged KV slice,
+then the LSE-weighted combine of all N shards' partials into the bf16 output.
+The other shards' partials are computed once before timing and stay resident
+in HBM, as they would after the exchange.  Inputs are synthetic (seeded normal
+bf16, shapes of the named workload) and resident in HBM before timing.
+
+Cold cache: the timed shards' KV pools are replicated until the copies exceed
+twice the 256 MB Infinity Cache, and step i reads copy i mod n, so each step
+streams its KV from HBM as a real decode step does (other layers evict it).
+
+Output: one JSON line (rank 0).  `value` is microseconds per decode step.
+The roofline object describes the dominant launch (the shard partial call),
+timed live with HIP events on the stream the library launches on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+MALL_BYTES = 256 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(case, r):
+    """Bytes the method must move for shard r's partial (KV once, q, outputs, tables)."""
+    w = case.w
+    ll = case.local_lens(r)
+    nblk = -(-ll // w.block_size)
+    if w.kind == "mla":
+        kv = int(ll.sum()) * w.dk * 2
+    else:
+        kv = int(ll.sum()) * w.kv_heads * w.head_dim * 2 * 2
+    q = w.batch * w.heads * w.dk * 2
+    out = w.batch * w.heads * (w.dv + 1) * 4
+    meta = int(nblk.sum()) * 4 + w.batch * 4
+    return kv + q + out + meta, kv
+
+
+def algorithmic_flops(case, r):
+    w = case.w
+    ll = int(case.local_lens(r).sum())
+    if w.kind == "mla":
+        return ll * w.heads * 2 * (w.dk + w.dv)
+    return ll * w.heads * 4 * w.head_dim
+
+
+def combine_bytes(w):
+    return w.num_shards * w.batch * w.heads * (w.dv + 1) * 4 + w.batch * w.heads * w.dv * 2
+
+
+def cpu_baseline(case, budget_s=12.0):
+    """The fp64 oracle on the host cores, on a bounded sample of the same step."""
+    import oracle
+    w = case.w
+    ranks = list(w.ranks)
+    # sample: requests in order until the budget is spent (at least one)
+    done_tokens = 0
+    total_tokens = sum(int(case.local_lens(r).sum()) for r in ranks)
+    t_spent = 0.0
+    reqs = 0
+    for b in range(w.batch):
+        q = oracle.widen_bf16(case.q[b])
+        parts = []
+        for r in range(w.num_shards):
+            L = int(case.seq_lens[b])
+            pos = oracle.shard_positions(L, w.num_shards, r, w.layout)
+            if r in ranks:
+                if w.kind == "mla":
+                    kv = oracle.widen_bf16(case.rows_at(b, pos)[0])
+                    t0 = time.perf_counter()
+                    parts.append(oracle.mla_attention(q, kv, w.scale, w.kv_lora_rank))
+                    t_spent += time.perf_counter() - t0
+                else:
+                    k, v = case.rows_at(b, pos)
+                    k, v = oracle.widen_bf16(k), oracle.widen_bf16(v)
+                    t0 = time.perf_counter()
+                    parts.append(oracle.gqa_attention(q, k, v, w.scale))
+                    t_spent += time.perf_counter() - t0
+                done_tokens += len(pos)
+            else:
+                parts.append((np.zeros((w.heads, w.dv)), np.full(w.heads, -np.inf)))
+        t0 = time.perf_counter()
+        oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        t_spent += time.perf_counter() - t0
+        reqs += 1
+        if t_spent >= budget_s:
+            break
+    frac = done_tokens / max(total_tokens, 1)
+    us_per_step = t_spent / max(frac, 1e-12) * 1e6
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {"value": round(us_per_step, 1), "unit": "us/step", "cores": min(cores, threads), "kind": "oracle",
+            "sample": f"{reqs} of {w.batch} requests ({frac * 100:.1f}% of the step's tokens), "
+                      f"fp64 numpy, {t_spent:.1f} s measured, scaled to one full step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c1", help="c0 c1 c2 c3 c4a c4b")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--warm-cache", action="store_true", help="no KV rotation (reported as such)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs one GPU only; the N shards are simulated on one device. "
+                                   "Run with --gpus 1."}))
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    from workloads.device import bf16_tensor, int32_tensor
+    from kv_cache_context_amd import ops
+
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    case = W.Case(w, seed=args.seed)
+    n = w.num_shards
+    mb = case.max_blocks_per_seq()
+    hint = max(1, case.max_seq_len)
+    log(f"[bench] workload {w.name}: {w.description}; seq_lens total {int(case.seq_lens.sum())}")
+
+    po = torch.empty((n, w.batch, w.heads, w.dv), dtype=torch.float32, device=dev)
+    pl = torch.empty((n, w.batch, w.heads), dtype=torch.float32, device=dev)
+    q_d = bf16_tensor(case.q, dev)
+    lens_d = int32_tensor(case.seq_lens, dev)
+    shards = {}
+    t0 = time.time()
+    caches = case.shards(range(n), max_blocks=mb)
+    for r in range(n):
+        sc = caches[r]
+        caches[r] = None
+        common = dict(block_size=w.block_size, max_blocks_per_seq=mb, num_blocks=sc.num_blocks, shard_rank=r,
+                      num_shards=n, layout=w.layout, max_seq_len_hint=hint, softmax_scale=w.scale)
+        ent = {"table": int32_tensor(sc.block_table, dev)}
+        if w.kind == "mla":
+            ent["p"] = ops.mla_params(batch=w.batch, num_heads=w.heads, **common)
+            ent["pools"] = [bf16_tensor(sc.pools[0], dev)]
+            ent["ws"] = ops.mla_workspace(ent["p"], dev)
+        else:
+            ent["p"] = ops.gqa_params(batch=w.batch, num_q_heads=w.heads, num_kv_heads=w.kv_heads, **common)
+            ent["pools"] = [(bf16_tensor(sc.pools[0], dev), bf16_tensor(sc.pools[1], dev))]
+            ent["ws"] = ops.gqa_workspace(ent["p"], dev)
+        del sc
+        shards[r] = ent
+
+    def partial(r, copy):
+        e = shards[r]
+        pool = e["pools"][copy]
+        st = torch.cuda.current_stream()
+        if w.kind == "mla":
+            ops.dcp_mla_decode_partial(e["p"], q_d, pool, e["table"], lens_d, po[r], pl[r], e["ws"], st)
+        else:
+            ops.dcp_gqa_decode_partial(e["p"], q_d, pool[0], pool[1], e["table"], lens_d, po[r], pl[r], e["ws"],
+                                       st)
+
+    for r in range(n):  # every shard's partial once: the resident inputs of the combine
+        partial(r, 0)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in {time.time() - t0:.1f} s")
+
+    timed = list(w.ranks)
+    kv_bytes_timed = sum(algorithmic_bytes(case, r)[1] for r in timed)
+    copies = 1
+    if not args.warm_cache and kv_bytes_timed > 0:
+        copies = min(64, max(1, math.ceil(2 * MALL_BYTES / kv_bytes_timed)))
+    for r in timed:
+        base = shards[r]["pools"][0]
+        for _ in range(copies - 1):
+            if w.kind == "mla":
+                shards[r]["pools"].append(base.clone())
+            else:
+                shards[r]["pools"].append((base[0].clone(), base[1].clone()))
+    torch.cuda.synchronize()
+    log(f"[bench] {copies} rotating copies of the timed KV ({kv_bytes_timed / 1e6:.1f} MB each)")
+
+    out_bf = torch.empty((w.batch, w.heads, w.dv), dtype=torch.bfloat16, device=dev)
+
+    def do_partials(i):
+        for r in timed:
+            partial(r, i % copies)
+
+    def do_combine(i):
+        ops.dcp_combine(po, pl, out_bf, None, None, torch.cuda.current_stream())
+
+    def step(i):
+        do_partials(i)
+        do_combine(i)
+
+    # Each timed region is K steps captured in one HIP graph and replayed once, so
+    # the device timeline has no host launch gaps; HIP events bracket the replay
+    # on the stream the kernels run on.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(args.warmup):
+            step(i)
+    torch.cuda.synchronize()
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(args.steps):
+                fn(i)
+        return g
+
+    def timed_replay(g, reps=3):
+        best = None
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(side):
+                e0.record(side)
+                g.replay()
+                e1.record(side)
+            e1.synchronize()
+            t = e0.elapsed_time(e1)
+            best = t if best is None else min(best, t)
+        return best
+
+    g_step = capture(step)
+    g_part = capture(do_partials)
+    g_comb = capture(do_combine)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        g_step.replay()  # warm the graph once
+    torch.cuda.synchronize()
+    total_ms = timed_replay(g_step, reps=1)
+    ms_per_step = total_ms / args.steps
+    part_ms = timed_replay(g_part)
+    comb_ms = timed_replay(g_comb)
+    part_mean = part_ms / args.steps * 1e3
+    comb_mean = comb_ms / args.steps * 1e3
+
+    alg_partial = sum(algorithmic_bytes(case, r)[0] for r in timed)
+    alg_comb = combine_bytes(w)
+    flops = sum(algorithmic_flops(case, r) for r in timed)
+    achieved = alg_partial / (part_mean * 1e-6) / 1e9
+    step_gbs = (alg_partial + alg_comb) / (ms_per_step * 1e-3) / 1e9
+
+    res = {
+        "metric": "us/decode step + achieved HBM GB/s (% peak), shard-local attn + combine",
+        "value": round(ms_per_step * 1e3, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "kind": w.kind, "batch": w.batch,
+                   "heads": w.heads, "num_shards": n, "timed_shards": timed, "block_size": w.block_size,
+                   "local_tokens": int(sum(case.local_lens(r).sum() for r in timed)),
+                   "kv_copies_rotated": copies},
+        "step_hbm_gbps": round(step_gbs, 1),
+        "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "partial_us": round(part_mean, 3),
+        "combine_us": round(comb_mean, 3),
+        "timing": "K steps captured in one HIP graph, replayed; HIP events around the replay",
+        "mfma_tflops": round(flops / (part_mean * 1e-6) / 1e12, 2),
+        "mfma_frac": round(flops / (part_mean * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "hbm", "kernel": f"dcp_{w.kind}_decode_partial",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": alg_partial},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

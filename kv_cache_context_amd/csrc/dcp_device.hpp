@@ -70,6 +70,26 @@ __device__ __forceinline__ void dma16(const void* src, DCP_LDS void* lds_wave_ba
 #pragma clang diagnostic pop
 }
 
+// Same copy with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit
+// byte offset (the saddr form): no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void dma16_sbase(const void* base, uint32_t voff, DCP_LDS void* lds_wave_base) {
+  const uint32_t m0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)lds_wave_base);
+  // build the 64-bit base from wave-uniform halves so it lands in an SGPR pair
+  const uint64_t b64 = (uint64_t)(uintptr_t)base;
+  const uint64_t sbase = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b64 >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b64);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(m0)
+      : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -79,53 +79,75 @@ __device__ __forceinline__ int find_request(const int* s_pref, int batch, int p)
   return uni(lo);
 }
 
-// Merge the split partials of one (request, head) row.  One wave per row;
-// lane i handles dv/64 consecutive outputs.  Writes the normalized output and
+// Merge the split partials of one (request, head) row.  One workgroup of
+// DV/2 threads per row, two output columns per thread.  The segment weights
+// are computed once into LDS, then every thread streams its columns of all
+// segments with independent loads (unrolled), so the merge is bandwidth- rather
+// than latency-bound even for many segments.  Writes the normalized output and
 // the natural-log LSE; a request with no local tokens gets (0, -inf).
 template <int DV>
-__device__ __forceinline__ void reduce_row(const SplitArgs& s, int heads, int b, int h) {
-  static_assert(DV % 256 == 0 || DV == 128, "dv");
-  constexpr int PER = DV / 64;  // floats per lane
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void reduce_row(const SplitArgs& s, int heads, int b, int h, float* s_w) {
+  constexpr int NT = DV / 2;
+  const int tid = threadIdx.x;
   const int geff = s.ws_meta[0];
   const int pb = s.ws_meta[1 + b], pe = s.ws_meta[2 + b];
   const int T = s.ws_meta[1 + s.batch];
-  float* orow = s.out + ((size_t)b * heads + h) * DV + lane * PER;
+  float* orow = s.out + ((size_t)b * heads + h) * DV + 2 * tid;
   if (pe <= pb || geff <= 0 || T <= 0) {
-#pragma unroll
-    for (int i = 0; i < PER; i += 4) *(f32x4*)(orow + i) = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (lane == 0) s.lse[(size_t)b * heads + h] = -__builtin_inff();
+    *(float2*)orow = make_float2(0.f, 0.f);
+    if (tid == 0) s.lse[(size_t)b * heads + h] = -__builtin_inff();
     return;
   }
   const int g0 = (int)(((int64_t)(pb + 1) * geff - 1) / T);
   const int g1 = (int)(((int64_t)pe * geff - 1) / T);
-  float M = -__builtin_inff();
-  for (int g = g0; g <= g1; ++g) M = fmaxf(M, s.ws_ml[((size_t)(g + b) * heads + h) * 2]);
-  float acc[PER];
+  if (g1 == g0) return;  // one workgroup held the whole request and wrote the result itself
+  const int nseg = g1 - g0 + 1;  // <= kMaxSplitWGs
+  // weights: max over segments, then exp2 of the shift, sum of weighted l
+  float mloc = -__builtin_inff();
+  for (int i = tid; i < nseg; i += NT) mloc = fmaxf(mloc, s.ws_ml[((size_t)(g0 + i + b) * heads + h) * 2]);
+  mloc = wave_max(mloc);
+  __shared__ float s_red[NT / 64];
+  if ((tid & 63) == 0) s_red[tid >> 6] = mloc;
+  __syncthreads();
+  float M = s_red[0];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  for (int i = 1; i < NT / 64; ++i) M = fmaxf(M, s_red[i]);
+  float lloc = 0.f;
+  for (int i = tid; i < nseg; i += NT) {
+    const size_t row = (size_t)(g0 + i + b) * heads + h;
+    const float wgt = exp2_fast((s.ws_ml[row * 2] - M) * s.c);
+    s_w[i] = wgt;
+    lloc += wgt * s.ws_ml[row * 2 + 1];
+  }
+  lloc = wave_sum(lloc);
+  __syncthreads();
+  if ((tid & 63) == 0) s_red[tid >> 6] = lloc;
+  __syncthreads();
   float Lsum = 0.f;
-  for (int g = g0; g <= g1; ++g) {
-    const size_t row = (size_t)(g + b) * heads + h;
-    const float mg = s.ws_ml[row * 2];
-    const float lg = s.ws_ml[row * 2 + 1];
-    const float w = exp2_fast((mg - M) * s.c);
-    Lsum += w * lg;
-    const float* src = s.ws_o + row * DV + lane * PER;
 #pragma unroll
-    for (int i = 0; i < PER; i += 4) {
-      const f32x4 x = *(const f32x4*)(src + i);
-      acc[i] += w * x[0];
-      acc[i + 1] += w * x[1];
-      acc[i + 2] += w * x[2];
-      acc[i + 3] += w * x[3];
+  for (int i = 0; i < NT / 64; ++i) Lsum += s_red[i];
+  float2 acc = make_float2(0.f, 0.f);
+  const float* src = s.ws_o + ((size_t)(g0 + b) * heads + h) * DV + 2 * tid;
+  const size_t seg_stride = (size_t)heads * DV;
+  int i = 0;
+  for (; i + 8 <= nseg; i += 8) {
+    float2 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = *(const float2*)(src + (size_t)(i + u) * seg_stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc.x += s_w[i + u] * x[u].x;
+      acc.y += s_w[i + u] * x[u].y;
     }
   }
+  for (; i < nseg; ++i) {
+    const float2 x = *(const float2*)(src + (size_t)i * seg_stride);
+    acc.x += s_w[i] * x.x;
+    acc.y += s_w[i] * x.y;
+  }
   const float inv = 1.f / Lsum;
-#pragma unroll
-  for (int i = 0; i < PER; i += 4)
-    *(f32x4*)(orow + i) = f32x4{acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv};
-  if (lane == 0) s.lse[(size_t)b * heads + h] = (M * s.c + __log2f(Lsum)) * kLn2;
+  *(float2*)orow = make_float2(acc.x * inv, acc.y * inv);
+  if (tid == 0) s.lse[(size_t)b * heads + h] = (M * s.c + __log2f(Lsum)) * kLn2;
 }
 
 }  // namespace dcp

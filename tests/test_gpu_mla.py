@@ -116,3 +116,13 @@ def test_c1_full(dev):
     """64 heads, 64K context, shard 1 of 8: every shard's partial and the combine."""
     say("c1 full")
     check_case(W.Case(W.WORKLOADS["c1"], seed=0), dev)
+
+
+@pytest.mark.parametrize("bs", [16, 48])
+def test_long_segment_table_window(dev, monkeypatch, bs):
+    """One workgroup walks > 1024 cache blocks of one request, so the staged
+    block-table window has to slide; small blocks also split tiles."""
+    monkeypatch.setenv("DCP_SPLIT_WGS", "1")
+    w = W.custom_workload(kind="mla", batch=2, heads=64, seq_lens=(70001, 33), num_shards=2, block_size=bs,
+                          wid=205)
+    check_case(W.Case(w, seed=6), dev)

@@ -324,38 +324,42 @@ class Case:
 
     def shard(self, r: int, max_blocks: int | None = None, threads: int | None = None) -> ShardCache:
         """Build shard r's pool(s) and table (host memory, bf16 bits)."""
+        return self.shards([r], max_blocks, threads)[0]
+
+    def shards(self, ranks, max_blocks: int | None = None, threads: int | None = None) -> list:
+        """Build several shards' pools in one pass over the generated K/V."""
         w = self.w
-        table, nb = self.block_table(r, max_blocks)
         B = w.block_size
-        pools = [np.zeros((nb, B) + self._row_shape(), np.uint16) for _ in self._tensor_ids()]
-        ll = self.local_lens(r)
-        jobs = []
-        for b in range(w.batch):
-            L = int(self.seq_lens[b])
-            for c in range(-(-L // CHUNK)):
-                jobs.append((b, c))
+        ranks = list(ranks)
+        out = []
+        for r in ranks:
+            table, nb = self.block_table(r, max_blocks)
+            pools = [np.zeros((nb, B) + self._row_shape(), np.uint16) for _ in self._tensor_ids()]
+            out.append(ShardCache(rank=r, local_lens=self.local_lens(r), block_table=table, pools=pools))
+        jobs = [(b, c) for b in range(w.batch) for c in range(-(-int(self.seq_lens[b]) // CHUNK))]
 
         def fill(job):
             b, c = job
             L = int(self.seq_lens[b])
-            pos = local_positions(L, w.num_shards, r, w.layout)
-            # local indices j whose global position falls in chunk c
             t0, t1 = c * CHUNK, min(L, (c + 1) * CHUNK)
-            if w.layout == ROUND_ROBIN:
-                j0 = len(range(r, t0, w.num_shards))
-                j1 = len(range(r, t1, w.num_shards))
-            else:
-                start = pos.start
-                j0 = min(max(t0 - start, 0), len(pos))
-                j1 = min(max(t1 - start, 0), len(pos))
-            if j1 <= j0:
-                return
-            j = np.arange(j0, j1)
-            g = np.asarray(pos[j0:j1], dtype=np.int64) - t0
-            blk = table[b, j // B]
-            off = j % B
-            for p, tid in zip(pools, self._tensor_ids()):
-                p[blk, off] = self._chunk(tid, b, c, L)[g]
+            chunks = [self._chunk(tid, b, c, L) for tid in self._tensor_ids()]
+            for sc in out:
+                r = sc.rank
+                pos = local_positions(L, w.num_shards, r, w.layout)
+                if w.layout == ROUND_ROBIN:
+                    j0 = len(range(r, t0, w.num_shards))
+                    j1 = len(range(r, t1, w.num_shards))
+                else:
+                    j0 = min(max(t0 - pos.start, 0), len(pos))
+                    j1 = min(max(t1 - pos.start, 0), len(pos))
+                if j1 <= j0:
+                    continue
+                j = np.arange(j0, j1)
+                g = np.asarray(pos[j0:j1], dtype=np.int64) - t0
+                blk = sc.block_table[b, j // B]
+                off = j % B
+                for p, a in zip(sc.pools, chunks):
+                    p[blk, off] = a[g]
 
         n = threads or _threads()
         if n > 1 and len(jobs) > 1:
@@ -364,7 +368,7 @@ class Case:
         else:
             for jb in jobs:
                 fill(jb)
-        return ShardCache(rank=r, local_lens=ll, block_table=table, pools=pools)
+        return out
 
 
 def random_partials(num_shards: int, batch: int, heads: int, dv: int, seed: int = 0,
