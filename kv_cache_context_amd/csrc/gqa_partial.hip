@@ -309,7 +309,11 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(GqaArgs a) {
 
 __global__ __launch_bounds__(D / 2) void reduce_kernel(GqaArgs a) {
   __shared__ float s_w[kMaxSplitWGs];
-  reduce_row<D>(a.s, a.hq, blockIdx.y, blockIdx.x, s_w);
+  const int rows = a.s.batch * a.hq;
+  for (int row = blockIdx.x; row < rows; row += gridDim.x) {
+    reduce_row<D>(a.s, a.hq, row / a.hq, row % a.hq, s_w);
+    __syncthreads();
+  }
 }
 
 }  // namespace gqa
@@ -319,7 +323,8 @@ hipError_t launch_gqa_partial(const GqaArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(gqa::partial_kernel, dim3(a.s.G, a.hkv / gqa::QH), dim3(gqa::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gqa::reduce_kernel, dim3(a.hq, a.s.batch), dim3(gqa::D / 2), 0, stream, a);
+  const int rows = a.s.batch * a.hq;
+  hipLaunchKernelGGL(gqa::reduce_kernel, dim3(rows < 1024 ? rows : 1024), dim3(gqa::D / 2), 0, stream, a);
   return hipGetLastError();
 }
 

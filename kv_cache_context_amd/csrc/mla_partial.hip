@@ -33,7 +33,11 @@ constexpr int R = 512, P = 64, DK = R + P;
 constexpr int ROW = DK * 2;           // bytes per latent row
 constexpr int TILE = 32;              // tokens per pipeline tile
 constexpr int STAGE = TILE * ROW;     // 36864 bytes
-constexpr int NST = 4;                // tiles resident in LDS
+#ifndef DCP_MLA_NST
+#define DCP_MLA_NST 4
+#endif
+constexpr int NST = DCP_MLA_NST;      // tiles resident in LDS (NST - 1 in flight)
+static_assert(NST >= 2 && NST <= 4, "ring depth");
 constexpr int CPR = ROW / 16;         // 16-byte chunks per row (72)
 constexpr int THREADS = 256;
 constexpr int DMA_N = TILE * CPR / THREADS;  // copies per thread per tile (9)
@@ -332,13 +336,15 @@ __device__ __attribute__((always_inline)) inline bool run_segment_body(
   barrier();
 
   copy_all(plan_copy(a, trow, sm, win, pg_hi, t0, tiles, true), goff, grow);
-  if (n > 1) copy_all(plan_copy(a, trow, sm, win, pg_hi, t0 + 1, tiles + STAGE, true), goff, grow);
-  if (n > 2) copy_all(plan_copy(a, trow, sm, win, pg_hi, t0 + 2, tiles + 2 * STAGE, true), goff, grow);
+#pragma unroll
+  for (int j = 1; j < NST - 1; ++j)
+    if (n > j) copy_all(plan_copy(a, trow, sm, win, pg_hi, t0 + j, tiles + j * STAGE, true), goff, grow);
   for (int i = 0; i < n; ++i) {
     const int k = t0 + i;
     const int rem = n - 1 - i;
-    if (rem >= 2) wait_vmcnt<2 * DMA_N>();
-    else if (rem == 1) wait_vmcnt<DMA_N>();
+    // copies issued after tile k: min(NST - 2, rem) tiles
+    if (NST >= 4 && rem >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * DMA_N>();
+    else if (NST >= 3 && rem >= 1) wait_vmcnt<DMA_N>();
     else wait_vmcnt<0>();
     barrier();
     DCP_LDS char* cur = tiles + (i % NST) * STAGE;
@@ -348,7 +354,8 @@ __device__ __attribute__((always_inline)) inline bool run_segment_body(
       wait_lgkm0();
       barrier();
     }
-    const TileCopy nxt = plan_copy(a, trow, sm, win, pg_hi, k + 3, tiles + ((i + 3) % NST) * STAGE, i + 3 < n);
+    const TileCopy nxt = plan_copy(a, trow, sm, win, pg_hi, k + NST - 1, tiles + ((i + NST - 1) % NST) * STAGE,
+                                   i + NST - 1 < n);
     if (active) compute_tile<EXACT>(cur, k * TILE, lr, i == 0, qf, acc, m, l, s.c, thr, ovf, nxt, goff, grow);
     else copy_all(nxt, goff, grow);
   }
@@ -433,9 +440,15 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
   }
 }
 
+// Rows (request, head) are visited grid-stride by a bounded grid, so a batch in
+// which no request was split costs a short launch, not one block per row.
 __global__ __launch_bounds__(R / 2) void reduce_kernel(MlaArgs a) {
   __shared__ float s_w[kMaxSplitWGs];
-  reduce_row<R>(a.s, a.heads, blockIdx.y, blockIdx.x, s_w);
+  const int rows = a.s.batch * a.heads;
+  for (int row = blockIdx.x; row < rows; row += gridDim.x) {
+    reduce_row<R>(a.s, a.heads, row / a.heads, row % a.heads, s_w);
+    __syncthreads();  // s_w is reused by the next row
+  }
 }
 
 }  // namespace mla
@@ -445,7 +458,8 @@ hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(mla::partial_kernel, dim3(a.s.G), dim3(mla::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla::reduce_kernel, dim3(a.heads, a.s.batch), dim3(mla::R / 2), 0, stream, a);
+  const int rows = a.s.batch * a.heads;
+  hipLaunchKernelGGL(mla::reduce_kernel, dim3(rows < 1024 ? rows : 1024), dim3(mla::R / 2), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -17,7 +17,7 @@ import os
 
 import torch  # noqa: F401  (loads the HIP runtime this library links against)
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdcp.so")
+LIB_PATH = os.environ.get("DCP_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdcp.so")
 
 DCP_OK = 0
 DCP_ERR_INVALID_ARGUMENT = 1

@@ -31,10 +31,10 @@ def say(*a):
 class ShardRun:
     """Device tensors and results of one shard's partial call."""
 
-    def __init__(self, case: W.Case, r: int, dev, stream=None, max_blocks=None, workspace=None):
+    def __init__(self, case: W.Case, r: int, dev, stream=None, max_blocks=None, workspace=None, cache=None):
         w = case.w
         self.case, self.r = case, r
-        sc = case.shard(r, max_blocks=max_blocks)
+        sc = cache if cache is not None else case.shard(r, max_blocks=max_blocks)
         self.sc = sc
         b = w.batch
         self.seq_lens = int32_tensor(case.seq_lens, dev)
@@ -66,6 +66,15 @@ class ShardRun:
             ops.dcp_gqa_decode_partial(self.p, self.q, self.k, self.v, self.table, self.seq_lens, out, lse,
                                        self.ws, self.stream)
         return out, lse
+
+
+def oracle_rows_merged(case: W.Case, b: int, heads):
+    """Oracle of the combined result built from the oracle's own shard partials
+    and merge (equal to unsharded attention: pinned by the merge invariant);
+    used where one request is too long to widen in one piece."""
+    w = case.w
+    parts = [oracle_rows(case, b, heads, r) for r in range(w.num_shards)]
+    return oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
 
 
 def oracle_rows(case: W.Case, b: int, heads, r: int | None):
