@@ -79,75 +79,89 @@ __device__ __forceinline__ int find_request(const int* s_pref, int batch, int p)
   return uni(lo);
 }
 
-// Merge the split partials of one (request, head) row.  One workgroup of
-// DV/2 threads per row, two output columns per thread.  The segment weights
-// are computed once into LDS, then every thread streams its columns of all
-// segments with independent loads (unrolled), so the merge is bandwidth- rather
-// than latency-bound even for many segments.  Writes the normalized output and
-// the natural-log LSE; a request with no local tokens gets (0, -inf).
+// Merge the split partials of request b, heads h0, h0 + hstep, ... .  A
+// workgroup of DV/2 threads serves one request: it reads the request's split
+// metadata once (a request held by one workgroup was written by the partial
+// kernel itself and is skipped here), then per head computes the segment
+// weights into LDS and streams its two output columns of every segment with
+// independent loads.  Writes the normalized output and the natural-log LSE;
+// a request with no local tokens gets (0, -inf).
 template <int DV>
-__device__ __forceinline__ void reduce_row(const SplitArgs& s, int heads, int b, int h, float* s_w) {
+__device__ __forceinline__ void reduce_request(const SplitArgs& s, int heads, int b, int h0, int hstep,
+                                               float* s_w) {
   constexpr int NT = DV / 2;
   const int tid = threadIdx.x;
   const int geff = s.ws_meta[0];
   const int pb = s.ws_meta[1 + b], pe = s.ws_meta[2 + b];
   const int T = s.ws_meta[1 + s.batch];
-  float* orow = s.out + ((size_t)b * heads + h) * DV + 2 * tid;
   if (pe <= pb || geff <= 0 || T <= 0) {
-    *(float2*)orow = make_float2(0.f, 0.f);
-    if (tid == 0) s.lse[(size_t)b * heads + h] = -__builtin_inff();
+    for (int h = h0; h < heads; h += hstep) {
+      *(float2*)(s.out + ((size_t)b * heads + h) * DV + 2 * tid) = make_float2(0.f, 0.f);
+      if (tid == 0) s.lse[(size_t)b * heads + h] = -__builtin_inff();
+    }
     return;
   }
   const int g0 = (int)(((int64_t)(pb + 1) * geff - 1) / T);
   const int g1 = (int)(((int64_t)pe * geff - 1) / T);
   if (g1 == g0) return;  // one workgroup held the whole request and wrote the result itself
   const int nseg = g1 - g0 + 1;  // <= kMaxSplitWGs
-  // weights: max over segments, then exp2 of the shift, sum of weighted l
-  float mloc = -__builtin_inff();
-  for (int i = tid; i < nseg; i += NT) mloc = fmaxf(mloc, s.ws_ml[((size_t)(g0 + i + b) * heads + h) * 2]);
-  mloc = wave_max(mloc);
   __shared__ float s_red[NT / 64];
-  if ((tid & 63) == 0) s_red[tid >> 6] = mloc;
-  __syncthreads();
-  float M = s_red[0];
+  for (int h = h0; h < heads; h += hstep) {
+    float mloc = -__builtin_inff();
+    for (int i = tid; i < nseg; i += NT) mloc = fmaxf(mloc, s.ws_ml[((size_t)(g0 + i + b) * heads + h) * 2]);
+    mloc = wave_max(mloc);
+    if ((tid & 63) == 0) s_red[tid >> 6] = mloc;
+    __syncthreads();
+    float M = s_red[0];
 #pragma unroll
-  for (int i = 1; i < NT / 64; ++i) M = fmaxf(M, s_red[i]);
-  float lloc = 0.f;
-  for (int i = tid; i < nseg; i += NT) {
-    const size_t row = (size_t)(g0 + i + b) * heads + h;
-    const float wgt = exp2_fast((s.ws_ml[row * 2] - M) * s.c);
-    s_w[i] = wgt;
-    lloc += wgt * s.ws_ml[row * 2 + 1];
-  }
-  lloc = wave_sum(lloc);
-  __syncthreads();
-  if ((tid & 63) == 0) s_red[tid >> 6] = lloc;
-  __syncthreads();
-  float Lsum = 0.f;
-#pragma unroll
-  for (int i = 0; i < NT / 64; ++i) Lsum += s_red[i];
-  float2 acc = make_float2(0.f, 0.f);
-  const float* src = s.ws_o + ((size_t)(g0 + b) * heads + h) * DV + 2 * tid;
-  const size_t seg_stride = (size_t)heads * DV;
-  int i = 0;
-  for (; i + 8 <= nseg; i += 8) {
-    float2 x[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = *(const float2*)(src + (size_t)(i + u) * seg_stride);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      acc.x += s_w[i + u] * x[u].x;
-      acc.y += s_w[i + u] * x[u].y;
+    for (int i = 1; i < NT / 64; ++i) M = fmaxf(M, s_red[i]);
+    float lloc = 0.f;
+    for (int i = tid; i < nseg; i += NT) {
+      const size_t row = (size_t)(g0 + i + b) * heads + h;
+      const float wgt = exp2_fast((s.ws_ml[row * 2] - M) * s.c);
+      s_w[i] = wgt;
+      lloc += wgt * s.ws_ml[row * 2 + 1];
     }
+    lloc = wave_sum(lloc);
+    __syncthreads();
+    if ((tid & 63) == 0) s_red[tid >> 6] = lloc;
+    __syncthreads();
+    float Lsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) Lsum += s_red[i];
+    float2 acc = make_float2(0.f, 0.f);
+    const float* src = s.ws_o + ((size_t)(g0 + b) * heads + h) * DV + 2 * tid;
+    const size_t seg_stride = (size_t)heads * DV;
+    int i = 0;
+    for (; i + 8 <= nseg; i += 8) {
+      float2 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = *(const float2*)(src + (size_t)(i + u) * seg_stride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc.x += s_w[i + u] * x[u].x;
+        acc.y += s_w[i + u] * x[u].y;
+      }
+    }
+    for (; i < nseg; ++i) {
+      const float2 x = *(const float2*)(src + (size_t)i * seg_stride);
+      acc.x += s_w[i] * x.x;
+      acc.y += s_w[i] * x.y;
+    }
+    const float inv = 1.f / Lsum;
+    *(float2*)(s.out + ((size_t)b * heads + h) * DV + 2 * tid) = make_float2(acc.x * inv, acc.y * inv);
+    if (tid == 0) s.lse[(size_t)b * heads + h] = (M * s.c + __log2f(Lsum)) * kLn2;
+    __syncthreads();  // s_w and s_red are reused by the next head
   }
-  for (; i < nseg; ++i) {
-    const float2 x = *(const float2*)(src + (size_t)i * seg_stride);
-    acc.x += s_w[i] * x.x;
-    acc.y += s_w[i] * x.y;
-  }
-  const float inv = 1.f / Lsum;
-  *(float2*)orow = make_float2(acc.x * inv, acc.y * inv);
-  if (tid == 0) s.lse[(size_t)b * heads + h] = (M * s.c + __log2f(Lsum)) * kLn2;
+}
+
+// Grid for the split reduce: blocks.y = requests, blocks.x = head strides
+// (enough blocks overall to cover the chip, one metadata read per block).
+inline dim3 reduce_grid(int batch, int heads) {
+  int per = 1024 / (batch > 0 ? batch : 1);
+  if (per < 1) per = 1;
+  if (per > heads) per = heads;
+  return dim3(per, batch);
 }
 
 }  // namespace dcp

@@ -309,11 +309,7 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(GqaArgs a) {
 
 __global__ __launch_bounds__(D / 2) void reduce_kernel(GqaArgs a) {
   __shared__ float s_w[kMaxSplitWGs];
-  const int rows = a.s.batch * a.hq;
-  for (int row = blockIdx.x; row < rows; row += gridDim.x) {
-    reduce_row<D>(a.s, a.hq, row / a.hq, row % a.hq, s_w);
-    __syncthreads();
-  }
+  reduce_request<D>(a.s, a.hq, blockIdx.y, blockIdx.x, gridDim.x, s_w);
 }
 
 }  // namespace gqa
@@ -323,8 +319,7 @@ hipError_t launch_gqa_partial(const GqaArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(gqa::partial_kernel, dim3(a.s.G, a.hkv / gqa::QH), dim3(gqa::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows = a.s.batch * a.hq;
-  hipLaunchKernelGGL(gqa::reduce_kernel, dim3(rows < 1024 ? rows : 1024), dim3(gqa::D / 2), 0, stream, a);
+  hipLaunchKernelGGL(gqa::reduce_kernel, reduce_grid(a.s.batch, a.hq), dim3(gqa::D / 2), 0, stream, a);
   return hipGetLastError();
 }
 

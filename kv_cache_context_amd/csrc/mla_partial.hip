@@ -444,11 +444,7 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
 // which no request was split costs a short launch, not one block per row.
 __global__ __launch_bounds__(R / 2) void reduce_kernel(MlaArgs a) {
   __shared__ float s_w[kMaxSplitWGs];
-  const int rows = a.s.batch * a.heads;
-  for (int row = blockIdx.x; row < rows; row += gridDim.x) {
-    reduce_row<R>(a.s, a.heads, row / a.heads, row % a.heads, s_w);
-    __syncthreads();  // s_w is reused by the next row
-  }
+  reduce_request<R>(a.s, a.heads, blockIdx.y, blockIdx.x, gridDim.x, s_w);
 }
 
 }  // namespace mla
@@ -458,8 +454,7 @@ hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(mla::partial_kernel, dim3(a.s.G), dim3(mla::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows = a.s.batch * a.heads;
-  hipLaunchKernelGGL(mla::reduce_kernel, dim3(rows < 1024 ? rows : 1024), dim3(mla::R / 2), 0, stream, a);
+  hipLaunchKernelGGL(mla::reduce_kernel, reduce_grid(a.s.batch, a.heads), dim3(mla::R / 2), 0, stream, a);
   return hipGetLastError();
 }
 

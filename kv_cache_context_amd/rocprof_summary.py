@@ -1,0 +1,80 @@
+"""Summaries of rocprofv3 output for the DCP kernels.
+
+    python -m kv_cache_context_amd.rocprof_summary stats <kernel_stats.csv>
+    python -m kv_cache_context_amd.rocprof_summary traffic <fetch counter_collection.csv> \
+        <write counter_collection.csv> <kernel name substring> <calibration copy bytes>
+
+`traffic` converts FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into bytes per
+launch of the named kernel, each scaled by the ratio between the known size of
+a plain device-to-device copy run in the same process (bench.py
+--calibration-copy) and what the same counter reports for that copy kernel.
+`source_hash()` fingerprints the kernel sources so a stored traffic figure is
+only used while the kernel it was measured on is unchanged.
+"""
+from __future__ import annotations
+
+import csv
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = {
+    "mla": ["csrc/mla_partial.hip", "csrc/dcp_device.hpp", "csrc/dcp_split.hpp", "csrc/dcp_internal.hpp", "build.py"],
+    "gqa": ["csrc/gqa_partial.hip", "csrc/dcp_device.hpp", "csrc/dcp_split.hpp", "csrc/dcp_internal.hpp", "build.py"],
+    "combine": ["csrc/combine.hip", "csrc/dcp_device.hpp", "csrc/dcp_internal.hpp", "build.py"],
+}
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stats(path: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = ["| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| {r['Name'][:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    return "\n".join(out)
+
+
+def _per_dispatch(path: str, counter: str):
+    vals = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int) -> dict:
+    res = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = _per_dispatch(path, name)
+        copy = [v for k, vs in vals.items() if k.startswith(COPY_KERNEL) for v in vs]
+        kern = [v for k, vs in vals.items() if kernel in k for v in vs]
+        if not copy or not kern:
+            raise SystemExit(f"missing dispatches for {name}: copy {len(copy)} kernel {len(kern)}")
+        copy_kib = max(copy)  # the calibration copy is the largest copy in the run
+        scale = copy_bytes / (copy_kib * 1024.0)
+        avg_kib = sum(kern) / len(kern)
+        res[name] = {"kib_per_dispatch": round(avg_kib, 1), "copy_kib": copy_kib, "scale": round(scale, 4),
+                     "bytes_per_launch": int(avg_kib * 1024 * scale), "dispatches": len(kern)}
+    res["bytes_per_launch"] = res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]
+    return res
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        print(stats(sys.argv[2]))
+    elif sys.argv[1] == "traffic":
+        print(json.dumps(traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5])), indent=1))
+    elif sys.argv[1] == "hash":
+        print(source_hash(sys.argv[2]))
