@@ -106,16 +106,31 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ float wave_max16(float v) {  // over lanes l, l^16, l^32, l^48
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// Reductions over the lanes l, l^16, l^32, l^48 (the four 16-lane rows of the
+// wave) with the gfx950 row-swap instructions: v_permlane16_swap exchanges odd
+// rows of one operand with even rows of the other and v_permlane32_swap the
+// upper half of one with the lower half of the other, so with both operands
+// holding v, the two results hold v and its partner lane's v in some order and
+// a commutative op of the two is the pairwise reduction.  Pure VALU: no LDS
+// round trip.
+__device__ __forceinline__ float row_swap16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float wave_sum16(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+__device__ __forceinline__ float row_swap32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float row_swap16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float row_swap32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wave_max16(float v) { return row_swap32_max(row_swap16_max(v)); }
+__device__ __forceinline__ float wave_sum16(float v) { return row_swap32_sum(row_swap16_sum(v)); }
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

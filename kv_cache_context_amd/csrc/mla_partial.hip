@@ -6,19 +6,26 @@
 // normalized partial attention and its natural-log LSE, merged across shards
 // by dcp_combine.
 //
-// Structure (per split workgroup of 4 waves, one per 16 query heads):
+// Structure (per split workgroup of 8 waves, two per SIMD):
 //  * The workgroup streams its tile range of the shard's paged cache from HBM
 //    into LDS with direct global->LDS copies (no register staging), 32 tokens
 //    (36 KiB) per tile, 4 tiles in LDS; every latent byte crosses HBM once for
-//    all 64 heads.
-//  * Scores, transposed: S^T[32 tok x 16 heads] = K_tile[32 x 576] . q^T with
+//    all heads.
+//  * Wave roles: wave w owns query heads 16*(w/2) .. +15 and half t = w%2 of
+//    the work on each tile: score rows 16t..16t+15 and value columns
+//    256t..256t+255.  Two waves share each SIMD, so one wave's LDS and MFMA
+//    latencies are covered by the other's instructions; the per-wave register
+//    budget (q for 16 heads, outputs for 256 columns) leaves room for deep
+//    operand prefetch windows.
+//  * Scores, transposed: S^T[16 tok x 16 heads] = K[16 x 576] . q^T with
 //    v_mfma_f32_16x16x32_bf16; the wave's q stays in registers for the whole
 //    segment.
-//  * Online softmax in base 2 (scale * log2 e folded into one FMA); the score
-//    tile layout puts one head per lane column, so the running max needs two
-//    cross-lane steps and the output rescale is lane-local.
-//  * Values, transposed: O^T[512 x 16 heads] += V^T[512 x 32 tok] . P^T with
-//    V^T read straight from the row-major tile by ds_read_b64_tr_b16.
+//  * Softmax in base 2 (scale * log2 e folded into one FMA) against a reference
+//    maximum shared by the two waves of a head block; the probabilities of the
+//    two token halves are exchanged through LDS (8 bytes per lane), so each
+//    wave then holds P^T for all 32 tokens of its heads.
+//  * Values, transposed: O^T[256 cols x 16 heads] += V^T[cols x 32 tok] . P^T
+//    with V^T read straight from the row-major tile by ds_read_b64_tr_b16.
 //  * LDS rows are 1152 B; 16-byte chunks are XOR-swizzled per row so both the
 //    row-wise K reads and the transposing V reads hit distinct banks.
 //  * Split-K partials go to the workspace and a small kernel merges them.
@@ -39,11 +46,13 @@ constexpr int STAGE = TILE * ROW;     // 36864 bytes
 constexpr int NST = DCP_MLA_NST;      // tiles resident in LDS (NST - 1 in flight)
 static_assert(NST >= 2 && NST <= 4, "ring depth");
 constexpr int CPR = ROW / 16;         // 16-byte chunks per row (72)
-constexpr int THREADS = 256;
-constexpr int DMA_N = TILE * CPR / THREADS;  // copies per thread per tile (9)
+constexpr int THREADS = 512;
+constexpr int NWAVE = THREADS / 64;
+constexpr int CPT = TILE * CPR / 64;  // 1 KiB copy instructions per tile (36)
+constexpr int DMA_N = (CPT + NWAVE - 1) / NWAVE;  // copy slots per wave (5; the last is partial)
 constexpr int KS = DK / 32;           // k-steps of the score contraction (18)
 constexpr int VB = R / 16;            // 16-column blocks of the value contraction (32)
-static_assert(TILE * CPR % THREADS == 0, "tile copy split");
+static_assert(TILE * CPR % 64 == 0, "tile copy split");
 
 // Chunk swizzle of LDS row r: 16-byte chunk c of row r is stored at chunk
 // (c & ~7) | ((c & 7) ^ swz(r)), so a row's 72 chunks stay inside their aligned
@@ -54,15 +63,24 @@ static_assert(TILE * CPR % THREADS == 0, "tile copy split");
 // transposing value reads (ds_read_b64_tr_b16, 16 rows x 2 chunks).
 __host__ __device__ constexpr int swz(int r) { return r & 7; }
 
-constexpr int TBL = 1024;  // block-table entries staged in LDS per window
+constexpr int TBL = 256;  // block-table entries staged in LDS per window
+
+// Exchange between the two waves of a head block: [head block][token half]
+struct Xchg {
+  float mx[4][2][16];  // tile maxima per head
+  uint2 p[4][2][64];   // per lane: 4 bf16 probabilities (one lane's MFMA operand half)
+  float l[4][2][16];   // segment sums per head
+};
 
 struct Smem {
   char tiles[NST * STAGE];
   int pref[kMaxBatch + 1];
   int tbl[TBL];
-  int wsum[THREADS / 64];
+  int wsum[NWAVE];
   int flag;
+  Xchg xc;
 };
+static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
 
 // Where the copies of one tile go: source block(s) and LDS stage.  All fields
 // are wave-uniform.
@@ -91,34 +109,68 @@ __device__ __forceinline__ void load_window(const MlaArgs& a, const int32_t* tro
   }
 }
 
-__device__ __forceinline__ TileCopy plan_copy(const MlaArgs& a, const int32_t* trow, Smem& sm, TableWin& win,
-                                              int pg_hi, int k, DCP_LDS char* stage, bool valid) {
+// Copy planner of one segment.  It plans the segment's tiles in order,
+// tracking the block and in-block row of the next tile incrementally (no
+// division per tile), and reads the next tile's block-table entries right
+// after a plan, so that LDS read has a whole tile of compute to land.
+struct Planner {
+  int pg, in;      // block and row offset of the next tile to plan
+  int pg_hi;       // one past the segment's last block
+  TableWin win;
+  int pf_pg;       // block whose table entries pf0 / pf1 hold; -1: none
+  int pf0, pf1;    // entries of blocks pf_pg and pf_pg + 1 (wave-uniform values)
+};
+
+__device__ __forceinline__ void plan_prefetch(Planner& pl, const Smem& sm) {
+  // indices clamped into the array; a value read for a block outside the
+  // window is never used (the next plan slides the window and drops it)
+  pl.pf0 = sm.tbl[min(max(pl.pg - pl.win.lo, 0), TBL - 1)];
+  pl.pf1 = sm.tbl[min(max(pl.pg + 1 - pl.win.lo, 0), TBL - 1)];
+  pl.pf_pg = pl.pg;
+}
+
+__device__ __forceinline__ TileCopy plan_next(const MlaArgs& a, const int32_t* trow, Smem& sm, Planner& pl,
+                                              DCP_LDS char* stage, bool valid) {
   TileCopy t;
   t.valid = valid;
   t.stage = stage;
   const SplitArgs& s = a.s;
   const int B = s.block_size;
-  const int tok0 = k * TILE;
-  const int pg0 = uni(tok0 / B);
-  const int in0 = tok0 - pg0 * B;
+  const int pg0 = pl.pg, in0 = pl.in;
   t.split = B - in0;
   int e0 = 0, e1 = 0;
   if (valid) {
     // rows past `split` need block pg0 + 1 only if the request has one; else
     // they are past the request's end (zeroed later) and read block pg0 again
-    const bool two = t.split < TILE && pg0 + 1 < pg_hi;
+    const bool two = t.split < TILE && pg0 + 1 < pl.pg_hi;
     const int need = two ? pg0 + 1 : pg0;
-    if (need >= win.end) {  // slide the window (rare: every TBL blocks)
+    if (need >= pl.win.end) {  // slide the window (rare: every TBL blocks)
       barrier();
-      load_window(a, trow, sm, pg0, pg_hi);
+      load_window(a, trow, sm, pg0, pl.pg_hi);
       wait_vmcnt<0>();
       wait_lgkm0();
       barrier();
-      win.lo = pg0;
-      win.end = min(pg_hi, pg0 + TBL);
+      pl.win.lo = pg0;
+      pl.win.end = min(pl.pg_hi, pg0 + TBL);
+      pl.pf_pg = -1;
     }
-    e0 = uni(sm.tbl[pg0 - win.lo]);
-    e1 = two ? uni(sm.tbl[pg0 + 1 - win.lo]) : e0;
+    if (pl.pf_pg == pg0) {
+      e0 = uni(pl.pf0);
+      e1 = two ? uni(pl.pf1) : e0;
+    } else {
+      e0 = uni(sm.tbl[pg0 - pl.win.lo]);
+      e1 = two ? uni(sm.tbl[pg0 + 1 - pl.win.lo]) : e0;
+    }
+    pl.in += TILE;  // at most two blocks per tile (block_size >= 16)
+    if (pl.in >= B) {
+      pl.in -= B;
+      ++pl.pg;
+      if (pl.in >= B) {
+        pl.in -= B;
+        ++pl.pg;
+      }
+    }
+    plan_prefetch(pl, sm);
   }
   const char* kv = (const char*)a.kv;
   t.base0 = kv + ((int64_t)e0 * B + in0) * ROW;
@@ -126,12 +178,15 @@ __device__ __forceinline__ TileCopy plan_copy(const MlaArgs& a, const int32_t* t
   return t;
 }
 
-// Issue copy i (0 <= i < DMA_N) of a planned tile: 1 KiB per wave.
+// Issue copy i (0 <= i < DMA_N) of a planned tile: 1 KiB per wave (chunks
+// 64 * (i * NWAVE + wave) .. +63 of the tile).
 __device__ __forceinline__ void copy_part(const TileCopy& t, int i, const int (&goff)[DMA_N],
                                           const int (&grow)[DMA_N]) {
   if (!t.valid) return;
   const int wave = uni(threadIdx.x >> 6);
-  DCP_LDS char* dst = t.stage + (i * (THREADS / 64) + wave) * 1024;
+  const int slot = i * NWAVE + wave;
+  if (slot >= CPT) return;  // the last round covers only part of the waves
+  DCP_LDS char* dst = t.stage + slot * 1024;
   if (t.split >= TILE) {
     dma16_sbase(t.base0, (uint32_t)goff[i], dst);
   } else {
@@ -152,148 +207,149 @@ __device__ __forceinline__ void zero_tail(DCP_LDS char* stage, int valid) {
     *(DCP_LDS f32x4*)(stage + c * 16) = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// One 32-token tile for the wave's 16 heads: scores, softmax, P.V.
-// EXACT = false: the softmax reference m is the segment's first-tile maximum
-//   and never moves; tiles whose maximum exceeds it by more than `thr` (p would
-//   pass 2^64) only raise `ovf`, and the caller recomputes the segment with
-//   EXACT = true.  No branch touches the output accumulators, so they stay in
-//   the matrix-core registers.
-// EXACT = true: classic online softmax, rescaling the output whenever the
-//   running maximum grows.
-template <bool EXACT>
-__device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int tok0, int lr, bool first,
-                                             const bf16x8 (&qf)[KS], f32x4 (&acc)[VB], float& m,
-                                             float& l, float c, float thr, bool& ovf,
+// One 32-token tile: this wave's scores over its 16 tokens for its 16 heads,
+// then (FULL) softmax and its 256 value columns over all 32 tokens.
+// FULL, reference not preset: the softmax reference m is the segment's
+//   first-tile maximum (over both token halves) and never moves; tiles whose
+//   maximum exceeds it by more than `thr` (p would pass 2^64) only raise `ovf`,
+//   and the caller then finds the segment's true maximum (MAXIMUM pass) and
+//   reruns with that reference preset, where p <= 1 everywhere.  No branch
+//   touches the output accumulators, so they need no rescaling.
+// MAXIMUM: scores only; m becomes the running maximum of this wave's half.
+// Every wave of the workgroup calls this with the same `first` and `preset`
+// (it holds workgroup barriers).
+enum { FULL = 0, MAXIMUM = 1 };
+template <int MODE>
+__device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int tok0, int lr, bool first, bool preset,
+                                             const bf16x8 (&qf)[KS], f32x4 (&acc)[VB / 2], float& m, float& l,
+                                             float c, float thr, bool& ovf, Xchg& xc, int th, int hq,
                                              const TileCopy& nxt, const int (&goff)[DMA_N],
                                              const int (&grow)[DMA_N]) {
   const int lane = threadIdx.x & 63;
   const int g4 = lane >> 4, r16 = lane & 15;
 
-  // ---- scores S^T[tok][head], two 16-token blocks.  K operands are read in
-  // groups of KG k-steps, one group ahead of the MFMAs that use them; the
-  // scheduling fences keep that shape (unbounded look-ahead spills registers).
-  const int fz = swz(r16);
+  // ---- scores S^T[tok][head] for tokens 16*th + (0..15): two MFMA chains
+  // (k-step parity); K operands stream through a window of KD k-steps.  The
+  // next tile's copies are spread over the steps.
+  const int fz = swz(r16);  // row 16*th + r16 has the swizzle of r16
   const int offE = ((g4) ^ fz) * 16;
   const int offO = ((4 | g4) ^ fz) * 16;
-  const DCP_LDS char* k0p = st + r16 * ROW;
-  const DCP_LDS char* k1p = st + (16 + r16) * ROW;
-  constexpr int KG = 3;
-  static_assert(KS % KG == 0, "k groups");
-  static_assert(KS / KG + VB / 8 >= DMA_N, "copy slots");
-  bf16x8 ka[2][KG], kb[2][KG];
-  auto load_group = [&](int grp, int buf) {
-#pragma unroll
-    for (int j = 0; j < KG; ++j) {
-      const int ks = grp * KG + j;
-      const int off = (ks >> 1) * 128 + ((ks & 1) ? offO : offE);
-      ka[buf][j] = *(const DCP_LDS bf16x8*)(k0p + off);
-      kb[buf][j] = *(const DCP_LDS bf16x8*)(k1p + off);
-    }
+  const DCP_LDS char* kp = st + (16 * th + r16) * ROW;
+  constexpr int KD = 8;
+  static_assert(2 * DMA_N <= KS, "copy slots");
+  bf16x8 kr[KD];
+  auto kload = [&](int ks) {
+    kr[ks % KD] = *(const DCP_LDS bf16x8*)(kp + (ks >> 1) * 128 + ((ks & 1) ? offO : offE));
   };
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-  load_group(0, 0);
 #pragma unroll
-  for (int grp = 0; grp < KS / KG; ++grp) {
+  for (int ks = 0; ks < KD; ++ks) kload(ks);
+  f32x4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
     __builtin_amdgcn_sched_barrier(0);
-    // the next tile's copies are spread over the MFMA groups so that their
-    // issue latency hides behind matrix work
-    copy_part(nxt, grp, goff, grow);
-    if (grp + 1 < KS / KG) load_group(grp + 1, (grp + 1) & 1);
-#pragma unroll
-    for (int j = 0; j < KG; ++j) {
-      s0 = mfma_16x16x32(ka[grp & 1][j], qf[grp * KG + j], s0);
-      s1 = mfma_16x16x32(kb[grp & 1][j], qf[grp * KG + j], s1);
-    }
+    if ((ks & 1) == 0 && ks / 2 < DMA_N) copy_part(nxt, ks / 2, goff, grow);
+    sc[ks & 1] = mfma_16x16x32(kr[ks % KD], qf[ks], sc[ks & 1]);
+    if (ks + KD < KS) kload(ks + KD);
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- online softmax (base 2).  Lane holds head r16, tokens 4*g4+i and 16+4*g4+i.
-  float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-  if (tok0 + TILE > lr) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int t = tok0 + (j < 4 ? 4 * g4 + j : 16 + 4 * g4 + (j - 4));
-      if (t >= lr) sv[j] = -__builtin_inff();
-    }
-  }
-  float mt = sv[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j) mt = fmaxf(mt, sv[j]);
-  mt = wave_max16(mt);
-  if constexpr (!EXACT) {
-    if (first) m = mt;
-    else ovf = ovf || (mt > m + thr);
-  } else {
-    const float mnew = fmaxf(m, mt);
-    const float alpha = exp2_fast((m - mnew) * c);  // 0 while m is still -inf
-    l *= alpha;
-    if (!__all(alpha == 1.f)) {
-#pragma unroll
-      for (int cb = 0; cb < VB; ++cb) acc[cb] *= alpha;
-    }
-    m = mnew;
-  }
-  const float mc = m * c;
-  float p[8];
-  float ps = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    p[j] = exp2_fast(fmaf(sv[j], c, -mc));
-    ps += p[j];
-  }
-  l += ps;
-  bf16x8 pt;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) pt[j] = (__bf16)p[j];
-
-  // ---- values O^T[col][head] += V^T[col][tok] . P^T[tok][head]
-  // V^T operands come from transposing LDS reads, VG column blocks per group,
-  // one group ahead of their MFMAs.
+  // V^T operands of the value contraction: issued now, so their LDS latency
+  // overlaps the softmax and the probability exchange.
   const int rowa = 4 * g4 + (r16 >> 2);
   const int fa = swz(rowa);
-  const int hb = (r16 & 3) >> 1;
+  const int hbit = (r16 & 3) >> 1;
   const int byte = (r16 & 1) * 8;
-  const DCP_LDS char* va = st + rowa * ROW + byte;
+  const DCP_LDS char* va = st + rowa * ROW + byte + th * (VB / 2 / 4) * 128;
   int voff[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) voff[q] = (((2 * q) | hb) ^ fa) * 16;
-  constexpr int VG = 4;
-  static_assert(VB % VG == 0, "v groups");
-  i16x4 vlo[2][VG], vhi[2][VG];
-  auto load_v = [&](int grp, int buf) {
-#pragma unroll
-    for (int j = 0; j < VG; ++j) {
-      const int cb = grp * VG + j;
-      const DCP_LDS char* p0 = va + (cb >> 2) * 128 + voff[cb & 3];
-      vlo[buf][j] = lds_read_tr16(p0);
-      vhi[buf][j] = lds_read_tr16(p0 + 16 * ROW);
-    }
+  for (int q = 0; q < 4; ++q) voff[q] = (((2 * q) | hbit) ^ fa) * 16;
+  constexpr int VD = 8;
+  i16x4 vlo[VD], vhi[VD];
+  auto vload = [&](int cb) {
+    const DCP_LDS char* p0 = va + (cb >> 2) * 128 + voff[cb & 3];
+    vlo[cb % VD] = lds_read_tr16(p0);
+    vhi[cb % VD] = lds_read_tr16(p0 + 16 * ROW);
   };
-  load_v(0, 0);
+  if constexpr (MODE == FULL) {
 #pragma unroll
-  for (int grp = 0; grp < VB / VG; ++grp) {
-    __builtin_amdgcn_sched_barrier(0);
-    if ((grp & 1) == 0 && KS / KG + grp / 2 < DMA_N) copy_part(nxt, KS / KG + grp / 2, goff, grow);
-    if (grp + 1 < VB / VG) load_v(grp + 1, (grp + 1) & 1);
+    for (int cb = 0; cb < VD; ++cb) vload(cb);
+  }
+
+  // ---- softmax (base 2).  Lane holds head r16, tokens 16*th + 4*g4 + i.
+  float sv[4];
 #pragma unroll
-    for (int j = 0; j < VG; ++j) {
-      const int cb = grp * VG + j;
-      const i16x8 v8 = __builtin_shufflevector(vlo[grp & 1][j], vhi[grp & 1][j], 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[cb] = mfma_16x16x32(__builtin_bit_cast(bf16x8, v8), pt, acc[cb]);
+  for (int i = 0; i < 4; ++i) sv[i] = sc[0][i] + sc[1][i];
+  if (tok0 + TILE > lr) {
+    const int t = tok0 + 16 * th + 4 * g4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (t + i >= lr) sv[i] = -__builtin_inff();
+  }
+  float mt = wave_max16(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+  if constexpr (MODE == MAXIMUM) {
+    m = fmaxf(m, mt);
+    return;
+  }
+  if (first && !preset) {
+    // the pair's maximum over the first tile sets the reference (token half 0
+    // of a segment's first tile always holds a valid token, so it is finite)
+    if (g4 == 0) xc.mx[hq][th][r16] = mt;
+    wait_lgkm0();
+    barrier();
+    m = fmaxf(mt, xc.mx[hq][th ^ 1][r16]);
+  } else if (!preset) {
+    ovf = ovf || (mt > m + thr);
+  }
+  bf16x4 own;
+  {
+    const float mc = m * c;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = exp2_fast(fmaf(sv[i], c, -mc));
+      ps += p;
+      own[i] = (__bf16)p;
     }
+    l += ps;
+    xc.p[hq][th][lane] = __builtin_bit_cast(uint2, own);
+  }
+  wait_lgkm0();
+  barrier();
+  // P^T operand over the 32 tokens: k-slots 0..3 hold tokens 4*g4 + i (half 0),
+  // slots 4..7 tokens 16 + 4*g4 + i (half 1), matching the V^T reads below.
+  bf16x8 pt;
+  {
+    const bf16x4 oth = __builtin_bit_cast(bf16x4, xc.p[hq][th ^ 1][lane]);
+    const bf16x4 lo = th ? oth : own;
+    const bf16x4 hi = th ? own : oth;
+    pt = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+
+  // ---- values O^T[col][head] += V^T[col][tok] . P^T[tok][head] for this wave's
+  // 256 columns; V^T operands stream through a window of VD column blocks.
+#pragma unroll
+  for (int cb = 0; cb < VB / 2; ++cb) {
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8 v8 = __builtin_bit_cast(
+        bf16x8, __builtin_shufflevector(vlo[cb % VD], vhi[cb % VD], 0, 1, 2, 3, 4, 5, 6, 7));
+    acc[cb] = mfma_16x16x32(v8, pt, acc[cb]);
+    if (cb + VD < VB / 2) vload(cb + VD);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool EXACT>
-__device__ __attribute__((always_inline)) inline bool run_segment_body(
-    const MlaArgs& a, Smem& sm, int b, int t0, int t1, int ntiles_b, int g) {
+// Runs the segment [t0, t1) of request b (tiles of the request).  FULL returns
+// true when the fixed softmax reference overflowed (nothing written then);
+// MAXIMUM stores the pair maximum of each head's scores in mref.
+template <int MODE>
+__device__ __attribute__((always_inline)) inline bool run_segment(
+    const MlaArgs& a, Smem& sm, int b, int t0, int t1, int ntiles_b, int g, bool preset, float& mref) {
   const SplitArgs& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int heads = a.heads;
-  const bool active = wave * 16 < heads;
+  const int th = uni(wave & 1), hq = uni(wave >> 1);
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int head = wave * 16 + r16;
+  const int head = 16 * hq + r16;
   DCP_LDS char* tiles = (DCP_LDS char*)sm.tiles;
   const float thr = 64.f / s.c;  // raw-score headroom of the fixed reference (p < 2^64)
   const int n = t1 - t0;
@@ -304,48 +360,67 @@ __device__ __attribute__((always_inline)) inline bool run_segment_body(
   int goff[DMA_N], grow[DMA_N];
 #pragma unroll
   for (int i = 0; i < DMA_N; ++i) {
-    const int slot = (i * (THREADS / 64) + wave) * 64 + lane;
+    const int slot = min(i * NWAVE + wave, CPT - 1) * 64 + lane;
     const int r = slot / CPR, ch = slot % CPR;
     grow[i] = r;
     goff[i] = r * ROW + ((ch ^ swz(r)) * 16);
   }
 
+  // q of this wave's 16 heads; heads past the request's count read as 0
+  // (their results are computed and dropped)
   bf16x8 qf[KS];
-  if (active) {
+  if (head < heads) {
     const bf16x8* qp = (const bf16x8*)(a.q + ((int64_t)b * heads + head) * DK + 8 * g4);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = qp[4 * ks];
-    // Make the compiler wait for q here, before any tile copy is in flight;
-    // otherwise its wait lands inside the tile loop and drains the prefetch.
+  } else {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16x8{};
   }
-  f32x4 acc[VB];
+  // Make the compiler wait for q here, before any tile copy is in flight;
+  // otherwise its wait lands inside the tile loop and drains the prefetch.
 #pragma unroll
-  for (int cb = 0; cb < VB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -__builtin_inff(), l = 0.f;
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  f32x4 acc[VB / 2];
+#pragma unroll
+  for (int cb = 0; cb < VB / 2; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = (MODE == FULL && preset) ? mref : -__builtin_inff();
+  float l = 0.f;
   bool ovf = false;
 
   // stage the segment's block-table entries: local blocks [pg_lo, pg_hi)
-  const int pg_lo = uni((t0 * TILE) / s.block_size);
-  const int pg_hi = uni(min(s.max_blocks, (min(t1 * TILE, lr) - 1) / s.block_size + 1));
-  TableWin win{pg_lo, min(pg_hi, pg_lo + TBL)};
-  load_window(a, trow, sm, pg_lo, pg_hi);
+  Planner pl;
+  pl.pg = uni((t0 * TILE) / s.block_size);
+  pl.in = t0 * TILE - pl.pg * s.block_size;
+  pl.pg_hi = uni(min(s.max_blocks, (min(t1 * TILE, lr) - 1) / s.block_size + 1));
+  pl.win.lo = pl.pg;
+  pl.win.end = min(pl.pg_hi, pl.pg + TBL);
+  load_window(a, trow, sm, pl.pg, pl.pg_hi);
   wait_vmcnt<0>();
   wait_lgkm0();
   barrier();
+  plan_prefetch(pl, sm);
 
-  copy_all(plan_copy(a, trow, sm, win, pg_hi, t0, tiles, true), goff, grow);
+  copy_all(plan_next(a, trow, sm, pl, tiles, true), goff, grow);
 #pragma unroll
   for (int j = 1; j < NST - 1; ++j)
-    if (n > j) copy_all(plan_copy(a, trow, sm, win, pg_hi, t0 + j, tiles + j * STAGE, true), goff, grow);
+    if (n > j) copy_all(plan_next(a, trow, sm, pl, tiles + j * STAGE, true), goff, grow);
+  // copy instructions this wave issues per tile: DMA_N, or one less where the
+  // last round of slots does not reach this wave
+  const bool full_round = uni(wave) + (DMA_N - 1) * NWAVE < CPT;
   for (int i = 0; i < n; ++i) {
     const int k = t0 + i;
     const int rem = n - 1 - i;
-    // copies issued after tile k: min(NST - 2, rem) tiles
-    if (NST >= 4 && rem >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * DMA_N>();
-    else if (NST >= 3 && rem >= 1) wait_vmcnt<DMA_N>();
-    else wait_vmcnt<0>();
+    // copies issued after tile k: those of min(NST - 2, rem) tiles
+    if (full_round) {
+      if (NST >= 4 && rem >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * DMA_N>();
+      else if (NST >= 3 && rem >= 1) wait_vmcnt<DMA_N>();
+      else wait_vmcnt<0>();
+    } else {
+      if (NST >= 4 && rem >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * (DMA_N - 1)>();
+      else if (NST >= 3 && rem >= 1) wait_vmcnt<DMA_N - 1>();
+      else wait_vmcnt<0>();
+    }
     barrier();
     DCP_LDS char* cur = tiles + (i % NST) * STAGE;
     const int valid = lr - k * TILE;
@@ -354,15 +429,22 @@ __device__ __attribute__((always_inline)) inline bool run_segment_body(
       wait_lgkm0();
       barrier();
     }
-    const TileCopy nxt = plan_copy(a, trow, sm, win, pg_hi, k + NST - 1, tiles + ((i + NST - 1) % NST) * STAGE,
-                                   i + NST - 1 < n);
-    if (active) compute_tile<EXACT>(cur, k * TILE, lr, i == 0, qf, acc, m, l, s.c, thr, ovf, nxt, goff, grow);
-    else copy_all(nxt, goff, grow);
+    const TileCopy nxt = plan_next(a, trow, sm, pl, tiles + ((i + NST - 1) % NST) * STAGE, i + NST - 1 < n);
+    compute_tile<MODE>(cur, k * TILE, lr, i == 0, preset, qf, acc, m, l, s.c, thr, ovf, sm.xc, th, hq, nxt, goff,
+                       grow);
   }
-  if constexpr (!EXACT) {
+  if constexpr (MODE == MAXIMUM) {
+    if (g4 == 0) sm.xc.mx[hq][th][r16] = m;
+    wait_lgkm0();
+    barrier();  // also: every wave is done with the tiles before they are refilled
+    mref = fmaxf(m, sm.xc.mx[hq][th ^ 1][r16]);
+    barrier();
+    return false;
+  }
+  if (!preset) {
     if (tid == 0) sm.flag = 0;
     barrier();
-    if (active && __any(ovf) && lane == 0) sm.flag = 1;
+    if (__any(ovf) && lane == 0) sm.flag = 1;
     barrier();
     const bool redo = uni(sm.flag) != 0;
     barrier();  // also: every wave is done with the tiles before they are refilled
@@ -371,21 +453,29 @@ __device__ __attribute__((always_inline)) inline bool run_segment_body(
     barrier();
   }
 
-  if (active) {
-    const float lt = wave_sum16(l);
+  // segment sums: each wave holds its own token half; the pair shares m
+  float lt = wave_sum16(l);
+  if (g4 == 0) sm.xc.l[hq][th][r16] = lt;
+  wait_lgkm0();
+  barrier();
+  lt += sm.xc.l[hq][th ^ 1][r16];
+  barrier();  // the exchange buffer is free again for the next segment
+
+  if (head < heads) {
+    const int col = th * (R / 2) + 4 * g4;
     if (t0 == 0 && t1 == ntiles_b) {
       // the whole request is in this workgroup: write the final result
       const float inv = 1.f / lt;
-      float* dst = s.out + ((size_t)b * heads + head) * R + 4 * g4;
+      float* dst = s.out + ((size_t)b * heads + head) * R + col;
 #pragma unroll
-      for (int cb = 0; cb < VB; ++cb) *(f32x4*)(dst + 16 * cb) = acc[cb] * inv;
-      if (g4 == 0) s.lse[(size_t)b * heads + head] = (m * s.c + __log2f(lt)) * kLn2;
+      for (int cb = 0; cb < VB / 2; ++cb) *(f32x4*)(dst + 16 * cb) = acc[cb] * inv;
+      if (th == 0 && g4 == 0) s.lse[(size_t)b * heads + head] = (m * s.c + __log2f(lt)) * kLn2;
     } else {
       const int slot = g + b;
-      float* dst = s.ws_o + ((size_t)slot * heads + head) * R + 4 * g4;
+      float* dst = s.ws_o + ((size_t)slot * heads + head) * R + col;
 #pragma unroll
-      for (int cb = 0; cb < VB; ++cb) *(f32x4*)(dst + 16 * cb) = acc[cb];
-      if (g4 == 0) {
+      for (int cb = 0; cb < VB / 2; ++cb) *(f32x4*)(dst + 16 * cb) = acc[cb];
+      if (th == 0 && g4 == 0) {
         float* ml = s.ws_ml + ((size_t)slot * heads + head) * 2;
         ml[0] = m;
         ml[1] = lt;
@@ -393,21 +483,6 @@ __device__ __attribute__((always_inline)) inline bool run_segment_body(
     }
   }
   return false;
-}
-
-template <bool EXACT>
-__device__ inline bool run_segment(const MlaArgs& a, Smem& sm, int b, int t0, int t1, int ntiles_b, int g);
-template <>
-__device__ __attribute__((always_inline)) inline bool run_segment<false>(
-    const MlaArgs& a, Smem& sm, int b, int t0, int t1, int ntiles_b, int g) {
-  return run_segment_body<false>(a, sm, b, t0, t1, ntiles_b, g);
-}
-// The exact path is rare; keep it out of line so its rescaling code does not
-// shape register allocation of the fast path.
-template <>
-__device__ __attribute__((noinline)) bool run_segment<true>(
-    const MlaArgs& a, Smem& sm, int b, int t0, int t1, int ntiles_b, int g) {
-  return run_segment_body<true>(a, sm, b, t0, t1, ntiles_b, g);
 }
 
 __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
@@ -432,8 +507,15 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
     if (pe > pb) {
       const int t0 = (p0 > pb ? p0 : pb) - pb;
       const int t1 = (p1 < pe ? p1 : pe) - pb;
-      if (run_segment<false>(a, sm, b, t0, t1, pe - pb, g))
-        run_segment<true>(a, sm, b, t0, t1, pe - pb, g);
+      // fixed-reference pass; on overflow, find the true maximum and run
+      // again with it preset (that run cannot overflow)
+      float mref = 0.f;
+      bool preset = false;
+      for (int pass = 0; pass < 2; ++pass) {
+        if (!run_segment<FULL>(a, sm, b, t0, t1, pe - pb, g, preset, mref)) break;
+        run_segment<MAXIMUM>(a, sm, b, t0, t1, pe - pb, g, false, mref);
+        preset = true;
+      }
     }
     if (pe >= p1 || b + 1 >= s.batch) break;
     ++b;
