@@ -3,6 +3,14 @@
     python -m kv_cache_context_amd.rocprof_summary stats <kernel_stats.csv>
     python -m kv_cache_context_amd.rocprof_summary traffic <fetch counter_collection.csv> \
         <write counter_collection.csv> <kernel name substring> <calibration copy bytes>
+    python -m kv_cache_context_amd.rocprof_summary report <prof dir> <workload> <mla|gqa>
+
+`report` writes the markdown summary of one workload's profiling runs (kernel
+trace statistics, the bench line of the traced run, and the counter traffic
+when the FETCH_SIZE / WRITE_SIZE runs exist) and prints the traffic entry for
+profiles/traffic.json.  The directory layout is the one of the commands quoted
+in the summary: <dir>/<wl>/kt_kernel_stats.csv, <dir>/<wl>_kt.log,
+<dir>/<wl>_FETCH_SIZE/p_counter_collection.csv, <dir>/<wl>_WRITE_SIZE/....
 
 `traffic` converts FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into bytes per
 launch of the named kernel, each scaled by the ratio between the known size of
@@ -71,6 +79,48 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int) -> dic
     return res
 
 
+CAL_COPY_BYTES = 1 << 30
+
+
+def report(prof: str, wl: str, kind: str) -> tuple[str, dict | None]:
+    kt_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {prof}/{wl} -o kt -- "
+              f"python -u bench.py --workload {wl}" + ("" if wl == "c1" else " --no-cpu-baseline"))
+    pmc_cmd = (f"rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d {prof}/{wl}_<counter> -o p -- "
+               f"python -u bench.py --workload {wl} --steps 5 --warmup 1 --no-cpu-baseline --calibration-copy")
+    bench = None
+    logp = os.path.join(prof, f"{wl}_kt.log")
+    if os.path.exists(logp):
+        for line in open(logp):
+            if line.startswith("{"):
+                bench = json.loads(line)
+    lines = [f"# {kind} partial + combine, workload {wl}", ""]
+    if bench:
+        lines += [f"Workload: {bench['config'].get('description', '')}", ""]
+    lines += ["Kernel trace (each step: the timed shards' partial calls, i.e. partial_kernel then its split",
+              "reduce, then one combine; warmup, capture and replay dispatches included):", "",
+              "```", kt_cmd, "```", "", stats(os.path.join(prof, wl, "kt_kernel_stats.csv")), ""]
+    if bench:
+        keep = {k: bench[k] for k in ("value", "unit", "partial_us", "combine_us", "step_hbm_gbps", "mfma_tflops")}
+        keep["roofline"] = {k: bench["roofline"][k] for k in ("achieved", "peak", "frac", "bytes_per_launch")}
+        lines += ["bench line of the traced run (HIP-event timing of graph replays; `partial_us` is one",
+                  "partial call = partial_kernel + reduce_kernel):", "", "```", json.dumps(keep), "```", ""]
+    entry = None
+    fetch = os.path.join(prof, f"{wl}_FETCH_SIZE", "p_counter_collection.csv")
+    write = os.path.join(prof, f"{wl}_WRITE_SIZE", "p_counter_collection.csv")
+    if os.path.exists(fetch) and os.path.exists(write):
+        t = traffic(fetch, write, f"{kind}::partial_kernel", CAL_COPY_BYTES)
+        lines += ["HBM traffic of partial_kernel from two counter runs (KiB per dispatch, scaled by the",
+                  "counter's reading for a 1 GiB device copy in the same process):", "", "```", pmc_cmd, "```", "",
+                  "| counter | KiB/dispatch | copy reads KiB | scale | bytes/launch |", "|---|---|---|---|---|"]
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            r = t[c]
+            lines.append(f"| {c} | {r['kib_per_dispatch']} | {r['copy_kib']} | {r['scale']} | {r['bytes_per_launch']} |")
+        lines += ["", f"Total: {t['bytes_per_launch']} bytes per launch."]
+        entry = {"bytes_per_launch": t["bytes_per_launch"], "fetch": t["FETCH_SIZE"]["bytes_per_launch"],
+                 "write": t["WRITE_SIZE"]["bytes_per_launch"], "source_hash": source_hash(kind)}
+    return "\n".join(lines) + "\n", entry
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         print(stats(sys.argv[2]))
@@ -78,3 +128,9 @@ if __name__ == "__main__":
         print(json.dumps(traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5])), indent=1))
     elif sys.argv[1] == "hash":
         print(source_hash(sys.argv[2]))
+    elif sys.argv[1] == "report":
+        text, entry = report(sys.argv[2], sys.argv[3], sys.argv[4])
+        out = os.path.join(os.path.dirname(PKG), "profiles", f"{sys.argv[4]}_partial_{sys.argv[3]}.md")
+        with open(out, "w") as f:
+            f.write(text)
+        print(json.dumps({f"{sys.argv[4]}:{sys.argv[3]}": entry}))
