@@ -85,6 +85,7 @@ dcp::SplitArgs split_args(int batch, int block_size, int max_blocks, int num_blo
   s.layout = (int)layout;
   s.G = 0;
   s.min_tiles = 1;
+  s.seg_cost = 0;
   s.scale = scale;
   s.c = scale * 1.4426950408889634f;
   return s;
@@ -164,6 +165,7 @@ dcp_status dcp_mla_decode_partial(const dcp_mla_params* p, const void* q, const 
   a.s.G = env_int("DCP_SPLIT_WGS", cus < dcp::kMaxSplitWGs ? cus : dcp::kMaxSplitWGs, 1,
                   dcp::kMaxSplitWGs);
   a.s.min_tiles = env_int("DCP_MLA_MIN_TILES", 8, 1, 1 << 20);
+  a.s.seg_cost = env_int("DCP_MLA_SEG_COST", 2, 0, 64);
   a.q = (const uint16_t*)q;
   a.kv = (const uint16_t*)kv_cache;
   a.heads = p->num_heads;
@@ -203,6 +205,7 @@ dcp_status dcp_gqa_decode_partial(const dcp_gqa_params* p, const void* q, const 
   if (g > dcp::kMaxSplitWGs) g = dcp::kMaxSplitWGs;
   a.s.G = env_int("DCP_SPLIT_WGS", g, 1, dcp::kMaxSplitWGs);
   a.s.min_tiles = env_int("DCP_GQA_MIN_TILES", 16, 1, 1 << 20);
+  a.s.seg_cost = env_int("DCP_GQA_SEG_COST", 0, 0, 64);
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k_cache;
   a.v = (const uint16_t*)v_cache;

@@ -43,6 +43,7 @@ struct SplitArgs {
   int batch, block_size, max_blocks, num_blocks, rank, nshards, layout;
   int G;          // split workgroups launched
   int min_tiles;  // fewest tiles a split workgroup is given
+  int seg_cost;   // tiles' worth of work charged for starting a request's segment
   float scale;    // softmax scale
   float c;        // softmax scale * log2(e)
 };

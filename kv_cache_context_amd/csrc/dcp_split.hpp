@@ -27,8 +27,12 @@ __device__ __forceinline__ int clamped_local_len(const SplitArgs& s, int b) {
   return uni(clamp_len(s, ld_uniform(s.seq_lens, b)));
 }
 
-// Fills s_pref[0..batch] with the inclusive prefix sums of tiles per request
-// (s_pref[0] = 0) and returns the total T.  All threads of the block call it.
+// Fills s_pref[0..batch] with the inclusive prefix sums of the requests' work
+// (s_pref[0] = 0) and returns the total T.  A request of n > 0 tiles weighs
+// n + seg_cost: the stream-K split then hands a workgroup that starts a
+// request (and pays its prologue: q, block-table window, pipeline fill) that
+// many fewer tiles.  Request b's tile k sits at position s_pref[b] + seg_cost + k.
+// All threads of the block call it.
 template <int THREADS>
 __device__ int plan_tiles(const SplitArgs& s, int tile, int* s_pref, int* s_wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -38,6 +42,7 @@ __device__ int plan_tiles(const SplitArgs& s, int tile, int* s_pref, int* s_wsum
     const int b = base + tid;
     int n = 0;
     if (b < s.batch) n = (clamp_len(s, s.seq_lens[b]) + tile - 1) / tile;
+    if (n > 0) n += s.seg_cost;
     int v = n;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -62,13 +67,28 @@ __device__ int plan_tiles(const SplitArgs& s, int tile, int* s_pref, int* s_wsum
   return uni(carry);
 }
 
+// Tiles [t0, t1) of request b (positions [pb, pe)) that fall in the workgroup's
+// positions [p0, p1); empty (t1 <= t0) when the range holds only the request's
+// charged start or nothing of it.
+struct SegTiles {
+  int t0, t1, ntiles;
+};
+__device__ __forceinline__ SegTiles seg_tiles(const SplitArgs& s, int pb, int pe, int p0, int p1) {
+  const int r0 = pb + s.seg_cost;  // position of tile 0
+  SegTiles t;
+  t.t0 = (p0 > r0 ? p0 : r0) - r0;
+  t.t1 = (p1 < pe ? p1 : pe) - r0;
+  t.ntiles = pe - r0;
+  return t;
+}
+
 __device__ __forceinline__ int split_wgs(const SplitArgs& s, int T) {
   if (T <= 0) return 0;
   const int want = (T + s.min_tiles - 1) / s.min_tiles;
   return want < s.G ? want : s.G;
 }
 
-// Largest b in [0, batch) with s_pref[b] <= p (the request holding tile p,
+// Largest b in [0, batch) with s_pref[b] <= p (the request holding position p,
 // skipping requests that have no tiles).
 __device__ __forceinline__ int find_request(const int* s_pref, int batch, int p) {
   int lo = 0, hi = batch - 1;
@@ -79,89 +99,236 @@ __device__ __forceinline__ int find_request(const int* s_pref, int batch, int p)
   return uni(lo);
 }
 
-// Merge the split partials of request b, heads h0, h0 + hstep, ... .  A
-// workgroup of DV/2 threads serves one request: it reads the request's split
-// metadata once (a request held by one workgroup was written by the partial
-// kernel itself and is skipped here), then per head computes the segment
-// weights into LDS and streams its two output columns of every segment with
-// independent loads.  Writes the normalized output and the natural-log LSE;
-// a request with no local tokens gets (0, -inf).
-template <int DV>
-__device__ __forceinline__ void reduce_request(const SplitArgs& s, int heads, int b, int h0, int hstep,
-                                               float* s_w) {
-  constexpr int NT = DV / 2;
-  const int tid = threadIdx.x;
+// ---------------------------------------------------------------- split reduce
+//
+// Request b's tiles [pb + seg_cost, pe) of the stream-K partition (T positions
+// over geff workgroups) were covered by workgroups g0..g1; workgroup g wrote the
+// un-normalized (m, l, o) of request b to slot g + b.  A request held by one
+// workgroup was finished by that workgroup and is skipped here; a request with
+// no local tokens gets (0, -inf).  The merge of segments i is
+//   M = max m_i, w_i = exp2((m_i - M) c), L = sum w_i l_i,
+//   o = sum w_i o_i / L, lse = (M c + log2 L) ln 2.
+// Two block mappings (blocks of REDUCE_THREADS = 4 waves), chosen by the host
+// from the launch shape; both give the same result:
+//  * by heads (many requests, few segments each): block (head group of 8,
+//    request); wave w merges heads w and w + 4 of the group, each lane DV/64
+//    columns, all segments.
+//  * by segments (few requests, many segments): block (column part, head,
+//    request); the 4 waves take every 4th segment and add their sums in LDS.
+constexpr int REDUCE_THREADS = 256;
+constexpr int kReduceHeads = 8;  // heads per block in the by-heads mapping
+
+struct SegRange {
+  int g0, nseg;  // first segment slot offset and segment count; nseg 0: empty request
+};
+
+__device__ __forceinline__ SegRange seg_range(const SplitArgs& s, int b) {
   const int geff = s.ws_meta[0];
   const int pb = s.ws_meta[1 + b], pe = s.ws_meta[2 + b];
   const int T = s.ws_meta[1 + s.batch];
-  if (pe <= pb || geff <= 0 || T <= 0) {
-    for (int h = h0; h < heads; h += hstep) {
-      *(float2*)(s.out + ((size_t)b * heads + h) * DV + 2 * tid) = make_float2(0.f, 0.f);
-      if (tid == 0) s.lse[(size_t)b * heads + h] = -__builtin_inff();
-    }
-    return;
-  }
-  const int g0 = (int)(((int64_t)(pb + 1) * geff - 1) / T);
+  if (pe <= pb || geff <= 0 || T <= 0) return {0, 0};
+  // workgroups holding the request's first and last tile
+  const int g0 = (int)(((int64_t)(pb + s.seg_cost + 1) * geff - 1) / T);
   const int g1 = (int)(((int64_t)pe * geff - 1) / T);
-  if (g1 == g0) return;  // one workgroup held the whole request and wrote the result itself
-  const int nseg = g1 - g0 + 1;  // <= kMaxSplitWGs
-  __shared__ float s_red[NT / 64];
-  for (int h = h0; h < heads; h += hstep) {
-    float mloc = -__builtin_inff();
-    for (int i = tid; i < nseg; i += NT) mloc = fmaxf(mloc, s.ws_ml[((size_t)(g0 + i + b) * heads + h) * 2]);
-    mloc = wave_max(mloc);
-    if ((tid & 63) == 0) s_red[tid >> 6] = mloc;
-    __syncthreads();
-    float M = s_red[0];
-#pragma unroll
-    for (int i = 1; i < NT / 64; ++i) M = fmaxf(M, s_red[i]);
-    float lloc = 0.f;
-    for (int i = tid; i < nseg; i += NT) {
-      const size_t row = (size_t)(g0 + i + b) * heads + h;
-      const float wgt = exp2_fast((s.ws_ml[row * 2] - M) * s.c);
-      s_w[i] = wgt;
-      lloc += wgt * s.ws_ml[row * 2 + 1];
+  return {g0, g1 - g0 + 1};
+}
+
+// Segment weights of heads h0 .. h0 + nh - 1 (nh <= kReduceHeads) into
+// s_w[j * kMaxSplitWGs + i], with s_M[j] = max m_i (raw score units) and
+// s_L[j] = sum w_i l_i.  Wave w handles heads j = w, w + 4.
+__device__ __forceinline__ void seg_weights(const SplitArgs& s, int heads, int b, const SegRange& r, int h0,
+                                            int nh, float* s_w, float* s_M, float* s_L) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int j = wave; j < nh; j += REDUCE_THREADS / 64) {
+    const int h = h0 + j;
+    float mx = -__builtin_inff();
+    for (int i = lane; i < r.nseg; i += 64) mx = fmaxf(mx, s.ws_ml[((size_t)(r.g0 + i + b) * heads + h) * 2]);
+    mx = wave_max(mx);
+    float L = 0.f;
+    for (int i = lane; i < r.nseg; i += 64) {
+      const size_t row = (size_t)(r.g0 + i + b) * heads + h;
+      const float w = exp2_fast((s.ws_ml[row * 2] - mx) * s.c);
+      s_w[j * kMaxSplitWGs + i] = w;
+      L += w * s.ws_ml[row * 2 + 1];
     }
-    lloc = wave_sum(lloc);
-    __syncthreads();
-    if ((tid & 63) == 0) s_red[tid >> 6] = lloc;
-    __syncthreads();
-    float Lsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < NT / 64; ++i) Lsum += s_red[i];
-    float2 acc = make_float2(0.f, 0.f);
-    const float* src = s.ws_o + ((size_t)(g0 + b) * heads + h) * DV + 2 * tid;
-    const size_t seg_stride = (size_t)heads * DV;
-    int i = 0;
-    for (; i + 8 <= nseg; i += 8) {
-      float2 x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = *(const float2*)(src + (size_t)(i + u) * seg_stride);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        acc.x += s_w[i + u] * x[u].x;
-        acc.y += s_w[i + u] * x[u].y;
-      }
+    L = wave_sum(L);
+    if (lane == 0) {
+      s_M[j] = mx;
+      s_L[j] = L;
     }
-    for (; i < nseg; ++i) {
-      const float2 x = *(const float2*)(src + (size_t)i * seg_stride);
-      acc.x += s_w[i] * x.x;
-      acc.y += s_w[i] * x.y;
+  }
+  __syncthreads();
+}
+
+template <int N>
+struct FVec {
+  float v[N];
+};
+template <int N>
+__device__ __forceinline__ FVec<N> load_cols(const float* p) {
+  FVec<N> r;
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      const float4 x = *(const float4*)(p + 4 * k);
+      r.v[4 * k] = x.x;
+      r.v[4 * k + 1] = x.y;
+      r.v[4 * k + 2] = x.z;
+      r.v[4 * k + 3] = x.w;
     }
-    const float inv = 1.f / Lsum;
-    *(float2*)(s.out + ((size_t)b * heads + h) * DV + 2 * tid) = make_float2(acc.x * inv, acc.y * inv);
-    if (tid == 0) s.lse[(size_t)b * heads + h] = (M * s.c + __log2f(Lsum)) * kLn2;
-    __syncthreads();  // s_w and s_red are reused by the next head
+  } else if constexpr (N == 2) {
+    const float2 x = *(const float2*)p;
+    r.v[0] = x.x;
+    r.v[1] = x.y;
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) r.v[k] = p[k];
+  }
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void store_cols(float* p, const FVec<N>& r) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k)
+      *(float4*)(p + 4 * k) = make_float4(r.v[4 * k], r.v[4 * k + 1], r.v[4 * k + 2], r.v[4 * k + 3]);
+  } else if constexpr (N == 2) {
+    *(float2*)p = make_float2(r.v[0], r.v[1]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) p[k] = r.v[k];
   }
 }
 
-// Grid for the split reduce: blocks.y = requests, blocks.x = head strides
-// (enough blocks overall to cover the chip, one metadata read per block).
-inline dim3 reduce_grid(int batch, int heads) {
-  int per = 1024 / (batch > 0 ? batch : 1);
-  if (per < 1) per = 1;
-  if (per > heads) per = heads;
-  return dim3(per, batch);
+struct ReduceSmem {
+  float w[kReduceHeads * kMaxSplitWGs];
+  float M[kReduceHeads], L[kReduceHeads];
+  float part[REDUCE_THREADS / 64][512];  // by-segments mapping: per-wave sums of a column part
+};
+
+// By heads: block (head group hg, request b).
+template <int DV>
+__device__ __forceinline__ void reduce_by_heads(const SplitArgs& s, int heads, int b, int hg, ReduceSmem& sm) {
+  constexpr int C = DV / 64;  // columns per lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h0 = hg * kReduceHeads;
+  const int nh = min(kReduceHeads, heads - h0);
+  const SegRange r = seg_range(s, b);
+  if (r.nseg == 1) return;  // finished by the workgroup that held it
+  if (r.nseg == 0) {
+    FVec<C> z;
+#pragma unroll
+    for (int k = 0; k < C; ++k) z.v[k] = 0.f;
+    for (int j = wave; j < nh; j += REDUCE_THREADS / 64) {
+      store_cols<C>(s.out + ((size_t)b * heads + h0 + j) * DV + lane * C, z);
+      if (lane == 0) s.lse[(size_t)b * heads + h0 + j] = -__builtin_inff();
+    }
+    return;
+  }
+  seg_weights(s, heads, b, r, h0, nh, sm.w, sm.M, sm.L);
+  const size_t stride = (size_t)heads * DV;
+  for (int j = wave; j < nh; j += REDUCE_THREADS / 64) {
+    const int h = h0 + j;
+    const float* src = s.ws_o + ((size_t)(r.g0 + b) * heads + h) * DV + lane * C;
+    const float* w = sm.w + j * kMaxSplitWGs;
+    FVec<C> acc;
+#pragma unroll
+    for (int k = 0; k < C; ++k) acc.v[k] = 0.f;
+    int i = 0;
+    for (; i + 4 <= r.nseg; i += 4) {
+      FVec<C> x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = load_cols<C>(src + (size_t)(i + u) * stride);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < C; ++k) acc.v[k] += w[i + u] * x[u].v[k];
+    }
+    for (; i < r.nseg; ++i) {
+      const FVec<C> x = load_cols<C>(src + (size_t)i * stride);
+#pragma unroll
+      for (int k = 0; k < C; ++k) acc.v[k] += w[i] * x.v[k];
+    }
+    const float inv = 1.f / sm.L[j];
+#pragma unroll
+    for (int k = 0; k < C; ++k) acc.v[k] *= inv;
+    store_cols<C>(s.out + ((size_t)b * heads + h) * DV + lane * C, acc);
+    if (lane == 0) s.lse[(size_t)b * heads + h] = (sm.M[j] * s.c + __log2f(sm.L[j])) * kLn2;
+  }
+}
+
+// By segments: block (column part cp of CP, head h, request b).
+template <int DV, int CP>
+__device__ __forceinline__ void reduce_by_segments(const SplitArgs& s, int heads, int b, int h, int cp,
+                                                   ReduceSmem& sm) {
+  constexpr int C = DV / CP / 64;  // columns per lane
+  static_assert(C >= 1 && DV / CP <= 512, "column part");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = cp * (DV / CP) + lane * C;
+  const SegRange r = seg_range(s, b);
+  if (r.nseg == 1) return;
+  if (r.nseg == 0) {
+    if (wave == 0) {
+      FVec<C> z;
+#pragma unroll
+      for (int k = 0; k < C; ++k) z.v[k] = 0.f;
+      store_cols<C>(s.out + ((size_t)b * heads + h) * DV + col, z);
+      if (lane == 0 && cp == 0) s.lse[(size_t)b * heads + h] = -__builtin_inff();
+    }
+    return;
+  }
+  seg_weights(s, heads, b, r, h, 1, sm.w, sm.M, sm.L);
+  const size_t stride = (size_t)heads * DV;
+  const float* src = s.ws_o + ((size_t)(r.g0 + b) * heads + h) * DV + col;
+  constexpr int NW = REDUCE_THREADS / 64;
+  FVec<C> acc;
+#pragma unroll
+  for (int k = 0; k < C; ++k) acc.v[k] = 0.f;
+  int i = wave;
+  for (; i + 3 * NW < r.nseg; i += 4 * NW) {
+    FVec<C> x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = load_cols<C>(src + (size_t)(i + u * NW) * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < C; ++k) acc.v[k] += sm.w[i + u * NW] * x[u].v[k];
+  }
+  for (; i < r.nseg; i += NW) {
+    const FVec<C> x = load_cols<C>(src + (size_t)i * stride);
+#pragma unroll
+    for (int k = 0; k < C; ++k) acc.v[k] += sm.w[i] * x.v[k];
+  }
+#pragma unroll
+  for (int k = 0; k < C; ++k) sm.part[wave][lane * C + k] = acc.v[k];
+  __syncthreads();
+  if (wave == 0) {
+    const float inv = 1.f / sm.L[0];
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) t += sm.part[q][lane * C + k];
+      acc.v[k] = t * inv;
+    }
+    store_cols<C>(s.out + ((size_t)b * heads + h) * DV + col, acc);
+    if (lane == 0 && cp == 0) s.lse[(size_t)b * heads + h] = (sm.M[0] * s.c + __log2f(sm.L[0])) * kLn2;
+  }
+}
+
+// Launch shape of the split reduce.  The by-segments mapping is used when the
+// workgroups outnumber the requests 16 to 1 or more (then a split request has
+// many segments); otherwise by heads.
+struct ReducePlan {
+  bool by_segments;
+  dim3 grid;
+};
+inline ReducePlan reduce_plan(int batch, int heads, int G, int col_parts) {
+  ReducePlan p;
+  p.by_segments = G >= 16 * batch;
+  if (p.by_segments) p.grid = dim3(col_parts, heads, batch);
+  else p.grid = dim3((heads + kReduceHeads - 1) / kReduceHeads, batch);
+  return p;
 }
 
 }  // namespace dcp

@@ -220,8 +220,6 @@ __device__ __forceinline__ void run_segment(const GqaArgs& a, Smem& sm, int quad
       qf[ks] = qp[4 * ks];
       if (!col_ok) qf[ks] = bf16x8{};
     }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
   f32x4 acc[VB];
 #pragma unroll
@@ -231,10 +229,14 @@ __device__ __forceinline__ void run_segment(const GqaArgs& a, Smem& sm, int quad
   const int pg_lo = uni((t0 * TILE) / s.block_size);
   const int pg_hi = uni(min(s.max_blocks, (min(t1 * TILE, lr) - 1) / s.block_size + 1));
   TableWin win{pg_lo, min(pg_hi, pg_lo + TBL)};
-  load_window(a, trow, sm, pg_lo, pg_hi);
+  load_window(a, trow, sm, pg_lo, pg_hi);  // in flight together with the q loads
   wait_vmcnt<0>();
   wait_lgkm0();
   barrier();
+  // q has arrived (vmcnt 0); tie it here so the compiler places no wait for it
+  // inside the tile loop, where it would drain the copy prefetch.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
 
   copy_all(plan_copy(a, trow, sm, win, pg_hi, quad, t0, tiles, true), voff);
   if (n > 1) copy_all(plan_copy(a, trow, sm, win, pg_hi, quad, t0 + 1, tiles + STAGE, true), voff);
@@ -297,19 +299,19 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(GqaArgs a) {
   int b = find_request(sm.pref, s.batch, p0);
   for (;;) {
     const int pb = uni(sm.pref[b]), pe = uni(sm.pref[b + 1]);
-    if (pe > pb) {
-      const int t0 = (p0 > pb ? p0 : pb) - pb;
-      const int t1 = (p1 < pe ? p1 : pe) - pb;
-      run_segment(a, sm, quad, b, t0, t1, pe - pb, g);
-    }
+    const SegTiles st = seg_tiles(s, pb, pe, p0, p1);
+    if (pe > pb && st.t1 > st.t0) run_segment(a, sm, quad, b, st.t0, st.t1, st.ntiles, g);
     if (pe >= p1 || b + 1 >= s.batch) break;
     ++b;
   }
 }
 
-__global__ __launch_bounds__(D / 2) void reduce_kernel(GqaArgs a) {
-  __shared__ float s_w[kMaxSplitWGs];
-  reduce_request<D>(a.s, a.hq, blockIdx.y, blockIdx.x, gridDim.x, s_w);
+constexpr int RED_COL_PARTS = 1;  // column parts of the by-segments reduce
+
+__global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(GqaArgs a, int by_segments) {
+  __shared__ ReduceSmem sm;
+  if (by_segments) reduce_by_segments<D, RED_COL_PARTS>(a.s, a.hq, blockIdx.z, blockIdx.y, blockIdx.x, sm);
+  else reduce_by_heads<D>(a.s, a.hq, blockIdx.y, blockIdx.x, sm);
 }
 
 }  // namespace gqa
@@ -319,7 +321,8 @@ hipError_t launch_gqa_partial(const GqaArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(gqa::partial_kernel, dim3(a.s.G, a.hkv / gqa::QH), dim3(gqa::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gqa::reduce_kernel, reduce_grid(a.s.batch, a.hq), dim3(gqa::D / 2), 0, stream, a);
+  const ReducePlan rp = reduce_plan(a.s.batch, a.hq, a.s.G, gqa::RED_COL_PARTS);
+  hipLaunchKernelGGL(gqa::reduce_kernel, rp.grid, dim3(REDUCE_THREADS), 0, stream, a, rp.by_segments ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -377,10 +377,6 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16x8{};
   }
-  // Make the compiler wait for q here, before any tile copy is in flight;
-  // otherwise its wait lands inside the tile loop and drains the prefetch.
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   f32x4 acc[VB / 2];
 #pragma unroll
   for (int cb = 0; cb < VB / 2; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -395,10 +391,14 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
   pl.pg_hi = uni(min(s.max_blocks, (min(t1 * TILE, lr) - 1) / s.block_size + 1));
   pl.win.lo = pl.pg;
   pl.win.end = min(pl.pg_hi, pl.pg + TBL);
-  load_window(a, trow, sm, pl.pg, pl.pg_hi);
+  load_window(a, trow, sm, pl.pg, pl.pg_hi);  // in flight together with the q loads
   wait_vmcnt<0>();
   wait_lgkm0();
   barrier();
+  // q has arrived (vmcnt 0); tie it here so the compiler places no wait for it
+  // inside the tile loop, where it would drain the copy prefetch.
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
   plan_prefetch(pl, sm);
 
   copy_all(plan_next(a, trow, sm, pl, tiles, true), goff, grow);
@@ -504,16 +504,15 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
   int b = find_request(sm.pref, s.batch, p0);
   for (;;) {
     const int pb = uni(sm.pref[b]), pe = uni(sm.pref[b + 1]);
-    if (pe > pb) {
-      const int t0 = (p0 > pb ? p0 : pb) - pb;
-      const int t1 = (p1 < pe ? p1 : pe) - pb;
+    const SegTiles st = seg_tiles(s, pb, pe, p0, p1);
+    if (pe > pb && st.t1 > st.t0) {
       // fixed-reference pass; on overflow, find the true maximum and run
       // again with it preset (that run cannot overflow)
       float mref = 0.f;
       bool preset = false;
       for (int pass = 0; pass < 2; ++pass) {
-        if (!run_segment<FULL>(a, sm, b, t0, t1, pe - pb, g, preset, mref)) break;
-        run_segment<MAXIMUM>(a, sm, b, t0, t1, pe - pb, g, false, mref);
+        if (!run_segment<FULL>(a, sm, b, st.t0, st.t1, st.ntiles, g, preset, mref)) break;
+        run_segment<MAXIMUM>(a, sm, b, st.t0, st.t1, st.ntiles, g, false, mref);
         preset = true;
       }
     }
@@ -522,11 +521,12 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
   }
 }
 
-// Rows (request, head) are visited grid-stride by a bounded grid, so a batch in
-// which no request was split costs a short launch, not one block per row.
-__global__ __launch_bounds__(R / 2) void reduce_kernel(MlaArgs a) {
-  __shared__ float s_w[kMaxSplitWGs];
-  reduce_request<R>(a.s, a.heads, blockIdx.y, blockIdx.x, gridDim.x, s_w);
+constexpr int RED_COL_PARTS = 2;  // column parts of the by-segments reduce
+
+__global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(MlaArgs a, int by_segments) {
+  __shared__ ReduceSmem sm;
+  if (by_segments) reduce_by_segments<R, RED_COL_PARTS>(a.s, a.heads, blockIdx.z, blockIdx.y, blockIdx.x, sm);
+  else reduce_by_heads<R>(a.s, a.heads, blockIdx.y, blockIdx.x, sm);
 }
 
 }  // namespace mla
@@ -536,7 +536,8 @@ hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(mla::partial_kernel, dim3(a.s.G), dim3(mla::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla::reduce_kernel, reduce_grid(a.s.batch, a.heads), dim3(mla::R / 2), 0, stream, a);
+  const ReducePlan rp = reduce_plan(a.s.batch, a.heads, a.s.G, mla::RED_COL_PARTS);
+  hipLaunchKernelGGL(mla::reduce_kernel, rp.grid, dim3(REDUCE_THREADS), 0, stream, a, rp.by_segments ? 1 : 0);
   return hipGetLastError();
 }
 
