@@ -164,7 +164,7 @@ dcp_status dcp_mla_decode_partial(const dcp_mla_params* p, const void* q, const 
                    workspace, wl);
   a.s.G = env_int("DCP_SPLIT_WGS", cus < dcp::kMaxSplitWGs ? cus : dcp::kMaxSplitWGs, 1,
                   dcp::kMaxSplitWGs);
-  a.s.min_tiles = env_int("DCP_MLA_MIN_TILES", 8, 1, 1 << 20);
+  a.s.min_tiles = env_int("DCP_MLA_MIN_TILES", 4, 1, 1 << 20);
   a.s.seg_cost = env_int("DCP_MLA_SEG_COST", 2, 0, 64);
   a.q = (const uint16_t*)q;
   a.kv = (const uint16_t*)kv_cache;

@@ -108,14 +108,15 @@ __device__ __forceinline__ int find_request(const int* s_pref, int batch, int p)
 // no local tokens gets (0, -inf).  The merge of segments i is
 //   M = max m_i, w_i = exp2((m_i - M) c), L = sum w_i l_i,
 //   o = sum w_i o_i / L, lse = (M c + log2 L) ln 2.
-// Two block mappings (blocks of REDUCE_THREADS = 4 waves), chosen by the host
+// Two block mappings (blocks of REDUCE_THREADS = 8 waves), chosen by the host
 // from the launch shape; both give the same result:
 //  * by heads (many requests, few segments each): block (head group of 8,
-//    request); wave w merges heads w and w + 4 of the group, each lane DV/64
-//    columns, all segments.
+//    request); wave w merges head w of the group, each lane DV/64 columns,
+//    all segments.
 //  * by segments (few requests, many segments): block (column part, head,
-//    request); the 4 waves take every 4th segment and add their sums in LDS.
-constexpr int REDUCE_THREADS = 256;
+//    request); the 8 waves take every 8th segment (8 loads in flight per
+//    lane) and add their sums in LDS.
+constexpr int REDUCE_THREADS = 512;
 constexpr int kReduceHeads = 8;  // heads per block in the by-heads mapping
 
 struct SegRange {
@@ -135,7 +136,7 @@ __device__ __forceinline__ SegRange seg_range(const SplitArgs& s, int b) {
 
 // Segment weights of heads h0 .. h0 + nh - 1 (nh <= kReduceHeads) into
 // s_w[j * kMaxSplitWGs + i], with s_M[j] = max m_i (raw score units) and
-// s_L[j] = sum w_i l_i.  Wave w handles heads j = w, w + 4.
+// s_L[j] = sum w_i l_i.  Wave w handles head j = w.
 __device__ __forceinline__ void seg_weights(const SplitArgs& s, int heads, int b, const SegRange& r, int h0,
                                             int nh, float* s_w, float* s_M, float* s_L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -284,13 +285,14 @@ __device__ __forceinline__ void reduce_by_segments(const SplitArgs& s, int heads
   FVec<C> acc;
 #pragma unroll
   for (int k = 0; k < C; ++k) acc.v[k] = 0.f;
+  constexpr int U = 8;
   int i = wave;
-  for (; i + 3 * NW < r.nseg; i += 4 * NW) {
-    FVec<C> x[4];
+  for (; i + (U - 1) * NW < r.nseg; i += U * NW) {
+    FVec<C> x[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) x[u] = load_cols<C>(src + (size_t)(i + u * NW) * stride);
+    for (int u = 0; u < U; ++u) x[u] = load_cols<C>(src + (size_t)(i + u * NW) * stride);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int k = 0; k < C; ++k) acc.v[k] += sm.w[i + u * NW] * x[u].v[k];
   }

@@ -521,7 +521,10 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
   }
 }
 
-constexpr int RED_COL_PARTS = 2;  // column parts of the by-segments reduce
+#ifndef DCP_MLA_RED_COL_PARTS
+#define DCP_MLA_RED_COL_PARTS 2
+#endif
+constexpr int RED_COL_PARTS = DCP_MLA_RED_COL_PARTS;  // column parts of the by-segments reduce
 
 __global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(MlaArgs a, int by_segments) {
   __shared__ ReduceSmem sm;
