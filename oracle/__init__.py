@@ -23,6 +23,9 @@ Every function follows a stated definition:
 * ``merge`` — the LSE-weighted merge of N partial results into the exact
   output (section 4.1, the AllGather + ReduceScatter step, which reweights
   partial outputs by their LSE values).
+* ``combine_vproj_gate`` — the merge followed by each head's value
+  up-projection and a sigmoid output gate, the epilogue fused into the DCP
+  combine on the Kimi K3 GB300 decode page.
 * ``bf16_rne`` — round-to-nearest-even cast of fp32 to bf16 (the output cast).
 
 Parity of every function here is pinned by the CPU tests in
@@ -38,6 +41,7 @@ from .attention import (  # noqa: F401
     mla_shard_partial,
     gqa_shard_partial,
     merge,
+    combine_vproj_gate,
     bf16_rne,
     bf16_rne_bits,
 )

@@ -131,6 +131,29 @@ def merge(o_parts, lse_parts):
     return o, lse
 
 
+def combine_vproj_gate(o_parts, lse_parts, w_uv_t, gate):
+    """DCP merge followed by the per-head value up-projection and a sigmoid
+    output gate, the epilogue that the Kimi K3 GB300 decode page fuses into its
+    combine kernel (DCP partials combined together with v-proj and gating).
+
+    o_parts [N, b, H, Dv] latent partials and lse_parts [N, b, H] as for
+    ``merge``; w_uv_t [H, Dvo, Dv] holds each head's up-projection with the
+    latent index last (row n of head h maps the latent vector to output
+    column n); gate [b, H, Dvo] holds gate logits.  Returns (y [b, H, Dvo],
+    lse [b, H]) with
+      o = merge(o_parts, lse_parts)[0]
+      y[b, h, n] = sigmoid(gate[b, h, n]) * sum_k o[b, h, k] * w_uv_t[h, n, k].
+    """
+    o, lse = merge(o_parts, lse_parts)
+    w = np.asarray(w_uv_t, dtype=np.float64)
+    g = np.asarray(gate, dtype=np.float64)
+    y = np.empty(g.shape)
+    for h in range(w.shape[0]):
+        y[:, h, :] = o[:, h, :] @ w[h].T
+    sig = 1.0 / (1.0 + np.exp(-g))
+    return sig * y, lse
+
+
 def bf16_rne_bits(x) -> np.ndarray:
     """fp32 -> bf16 bit patterns, round to nearest, ties to even.
 

@@ -15,7 +15,11 @@ the implementation disagrees with:
   shard gives attention over the surviving tokens, the merge is associative,
   token order does not matter, adding a constant to all scores shifts only the
   LSE (also at magnitudes where an unshifted exp overflows);
-* MLA absorbed form equal to explicit per-head up-projection.
+* MLA absorbed form equal to explicit per-head up-projection;
+* the fused combine epilogue (merge, value up-projection, sigmoid gate):
+  a column-selecting projection with a saturated gate returns columns of the
+  plain merge, a zero gate halves the projection, and torch's batched fp64
+  matmul and sigmoid give the same result.
 
 ``tests/test_oracle_mutants.py`` plants mistakes in copies of the oracle and
 checks that each one fails at least one pin.
@@ -334,6 +338,60 @@ def pin_bf16_cast(impl):
     # widening is exact
     w = impl.widen_bf16(ref)
     assert np.array_equal(w, torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+def _vproj_case(r, N=3, b=4, H=3, Dv=20, Dvo=6):
+    o = r.standard_normal((N, b, H, Dv))
+    lse = r.standard_normal((N, b, H)) * 2.0
+    lse[0, 1, 2] = -np.inf
+    lse[:, 3, 0] = -np.inf  # an all-empty row
+    w = r.standard_normal((H, Dvo, Dv))
+    g = r.standard_normal((b, H, Dvo))
+    return o, lse, w, g
+
+
+def pin_vproj_selection(impl):
+    """Projection rows that pick latent columns, gate logits of 60 (sigmoid is
+    1 to 1e-26): the result is those columns of the plain merge, per head."""
+    r = _rng(41)
+    o, lse, _, _ = _vproj_case(r)
+    N, b, H, Dv = o.shape
+    cols = [[3, 0, 19, 7, 7, 11], [1, 2, 3, 4, 5, 6], [19, 18, 0, 1, 10, 9]]
+    w = np.zeros((H, 6, Dv))
+    for h in range(H):
+        for n, c in enumerate(cols[h]):
+            w[h, n, c] = 1.0
+    y, lse2 = impl.combine_vproj_gate(o, lse, w, np.full((b, H, 6), 60.0))
+    om, lm = impl.merge(o, lse)
+    _close(lse2, lm, what="vproj lse")
+    for h in range(H):
+        _close(y[:, h, :], om[:, h, cols[h]], what=f"vproj selection head {h}")
+
+
+def pin_vproj_gate_half(impl):
+    """Zero gate logits halve the projection; a gate logit g scales by 1/(1+e^-g)."""
+    r = _rng(42)
+    o, lse, w, _ = _vproj_case(r)
+    b, H, Dvo = o.shape[1], o.shape[2], w.shape[1]
+    y0, _ = impl.combine_vproj_gate(o, lse, w, np.zeros((b, H, Dvo)))
+    y1, _ = impl.combine_vproj_gate(o, lse, w, np.full((b, H, Dvo), 60.0))
+    _close(y0, 0.5 * y1, what="zero gate")
+    ym, _ = impl.combine_vproj_gate(o, lse, w, np.full((b, H, Dvo), -math.log(3.0)))
+    _close(ym, 0.25 * y1, what="gate logit -ln 3")
+
+
+def pin_vproj_torch(impl):
+    """torch fp64: bmm over heads of the merged latent with the transposed
+    projection, times torch.sigmoid of the gate."""
+    import torch
+    r = _rng(43)
+    o, lse, w, g = _vproj_case(r)
+    om, _ = impl.merge(o, lse)
+    ot = torch.from_numpy(np.ascontiguousarray(om.transpose(1, 0, 2)))           # [H, b, Dv]
+    wt = torch.from_numpy(np.ascontiguousarray(w.transpose(0, 2, 1)))            # [H, Dv, Dvo]
+    ref = torch.bmm(ot, wt).numpy().transpose(1, 0, 2) * torch.sigmoid(torch.from_numpy(g)).numpy()
+    y, _ = impl.combine_vproj_gate(o, lse, w, g)
+    _close(y, ref, tol=1e-11, what="vproj vs torch")
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

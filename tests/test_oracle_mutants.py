@@ -41,6 +41,10 @@ MUTANTS = {
                       "b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(8)"),
     "empty slice lse 0": ("return np.zeros((H, v.shape[1])), np.full(H, -np.inf)",
                           "return np.zeros((H, v.shape[1])), np.zeros(H)"),
+    "vproj untransposed": ("y[:, h, :] = o[:, h, :] @ w[h].T", "y[:, h, :] = (o[:, h, :] @ w[h].T[::-1])[:, ::-1]"),
+    "vproj wrong head": ("y[:, h, :] = o[:, h, :] @ w[h].T", "y[:, h, :] = o[:, h, :] @ w[(h + 1) % w.shape[0]].T"),
+    "gate sign": ("sig = 1.0 / (1.0 + np.exp(-g))", "sig = 1.0 / (1.0 + np.exp(g))"),
+    "gate missing": ("return sig * y, lse", "return y, lse"),
 }
 
 

@@ -48,7 +48,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # tensor ids inside the RNG key
-T_Q, T_KV, T_K, T_V, T_LEN, T_PERM, T_PART_O, T_PART_LSE = 1, 2, 3, 4, 5, 6, 7, 8
+T_Q, T_KV, T_K, T_V, T_LEN, T_PERM, T_PART_O, T_PART_LSE, T_WUV, T_GATE = 1, 2, 3, 4, 5, 6, 7, 8, 9, 10
 CHUNK = 1 << 16  # global token positions per RNG chunk
 
 ROUND_ROBIN = 0
@@ -387,3 +387,14 @@ def random_partials(num_shards: int, batch: int, heads: int, dv: int, seed: int 
         lse[mask] = -np.inf
         o[mask] = 0.0
     return o, lse
+
+
+def random_vproj(batch: int, heads: int, dvo: int, dv: int, seed: int = 0):
+    """Synthetic value up-projection and gate logits for the fused combine
+    epilogue, as bf16 bit patterns: w_uv_t [heads][dvo][dv] ~ N(0, 1/dv) (so
+    projected outputs stay O(1)) and gate [batch][heads][dvo] ~ N(0, 1)."""
+    rw = np.random.default_rng([seed, 98, T_WUV])
+    w = rw.standard_normal((heads, dvo, dv), dtype=np.float32) * np.float32(1.0 / math.sqrt(dv))
+    rg = np.random.default_rng([seed, 98, T_GATE])
+    g = rg.standard_normal((batch, heads, dvo), dtype=np.float32)
+    return f32_to_bf16_bits(w), f32_to_bf16_bits(g)
