@@ -83,6 +83,15 @@ def combine_bytes(w):
     return w.num_shards * w.batch * w.heads * (w.dv + 1) * 4 + w.batch * w.heads * w.dv * 2
 
 
+VPROJ_DVO = 128  # projected head width of the fused epilogue
+
+
+def vproj_bytes(w):
+    """Fused combine epilogue: partials + LSEs in, projection weights, gate logits, bf16 out."""
+    return (w.num_shards * w.batch * w.heads * (w.dv + 1) * 4 + w.heads * VPROJ_DVO * w.dv * 2
+            + 2 * w.batch * w.heads * VPROJ_DVO * 2)
+
+
 def cpu_baseline(case, budget_s=10.0):
     """The fp64 oracle on the host cores, on a bounded sample of the same step.
 
@@ -151,6 +160,9 @@ def main():
     ap.add_argument("--workload", default="c1", help="c0 c1 c2 c3 c4a c4b")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--epilogue", choices=("combine", "vproj"), default="combine",
+                    help="step epilogue: LSE combine + bf16 cast, or the combine fused with the per-head value "
+                         "up-projection (128 wide) and sigmoid gate (MLA workloads)")
     ap.add_argument("--warm-cache", action="store_true", help="no KV rotation (reported as such)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
@@ -235,8 +247,19 @@ def main():
         for r in timed:
             partial(r, i % copies)
 
+    if args.epilogue == "vproj":
+        if w.kind != "mla":
+            print(json.dumps({"error": "--epilogue vproj applies to the MLA workloads"}))
+            sys.exit(2)
+        w_bits, g_bits = W.random_vproj(w.batch, w.heads, VPROJ_DVO, w.dv, seed=args.seed)
+        w_uv_d, gate_d = bf16_tensor(w_bits, dev), bf16_tensor(g_bits, dev)
+        out_bf = torch.empty((w.batch, w.heads, VPROJ_DVO), dtype=torch.bfloat16, device=dev)
+
     def do_combine(i):
-        ops.dcp_combine(po, pl, out_bf, None, None, torch.cuda.current_stream())
+        if args.epilogue == "vproj":
+            ops.dcp_combine_vproj_gate(po, pl, w_uv_d, gate_d, out_bf, None, None, torch.cuda.current_stream())
+        else:
+            ops.dcp_combine(po, pl, out_bf, None, None, torch.cuda.current_stream())
 
     def step(i):
         do_partials(i)
@@ -288,7 +311,7 @@ def main():
     comb_mean = comb_ms / args.steps * 1e3
 
     alg_partial = sum(algorithmic_bytes(case, r)[0] for r in timed)
-    alg_comb = combine_bytes(w)
+    alg_comb = vproj_bytes(w) if args.epilogue == "vproj" else combine_bytes(w)
     flops = sum(algorithmic_flops(case, r) for r in timed)
     achieved = alg_partial / (part_mean * 1e-6) / 1e9
     step_gbs = (alg_partial + alg_comb) / (ms_per_step * 1e-3) / 1e9
@@ -314,6 +337,8 @@ def main():
         "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "partial_us": round(part_mean, 3),
         "combine_us": round(comb_mean, 3),
+        "epilogue": "dcp_combine_vproj_gate" if args.epilogue == "vproj" else "dcp_combine",
+        "epilogue_gbps": round(alg_comb / (comb_mean * 1e-6) / 1e9, 1),
         "timing": "K steps captured in one HIP graph, replayed; HIP events around the replay",
         "mfma_tflops": round(flops / (part_mean * 1e-6) / 1e12, 2),
         "mfma_frac": round(flops / (part_mean * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -17,6 +17,8 @@
  *                           consecutive groups of query heads; section 5.4)
  *   dcp_combine             the LSE-weighted merge of N partials, fused with
  *                           the cast of the result to bf16
+ *   dcp_combine_vproj_gate  the same merge fused with each head's value
+ *                           up-projection and a sigmoid output gate
  *
  * On one GPU the N ranks are simulated as N disjoint slices resident in the
  * same HBM; the cross-GPU exchange is not part of this library.
@@ -175,6 +177,33 @@ dcp_status dcp_gqa_decode_partial(const dcp_gqa_params* p, const void* q, const 
 dcp_status dcp_combine(int32_t num_shards, int32_t batch, int32_t num_heads, int32_t head_dim_v,
                        const float* partial_out, const float* partial_lse, void* out_bf16,
                        float* out_f32, float* lse_out, hipStream_t stream);
+
+/* The merge of dcp_combine fused with the epilogue that follows it in an MLA
+ * decode layer: each head's value up-projection (latent width head_dim_v to
+ * out_dim) and a sigmoid output gate.  The Kimi K3 GB300 decode page describes
+ * its DCP step as one kernel that combines the partial results together with
+ * the value projection and the gating.  For every (b, h), with o the merged
+ * latent row and lse* the merged LSE of dcp_combine:
+ *     y[n] = sigmoid(gate[b][h][n]) * sum_k o[k] * w_uv_t[h][n][k]
+ * (sigmoid factor 1 when gate is NULL).  o enters the product rounded to bf16;
+ * the product accumulates in fp32.
+ *
+ *  partial_out  fp32 [num_shards][batch][num_heads][head_dim_v]
+ *  partial_lse  fp32 [num_shards][batch][num_heads]
+ *  w_uv_t       bf16 [num_heads][out_dim][head_dim_v]  (latent index contiguous)
+ *  gate         bf16 [batch][num_heads][out_dim] gate logits, or NULL
+ *  out_bf16     bf16 [batch][num_heads][out_dim] or NULL
+ *  out_f32      fp32 [batch][num_heads][out_dim] or NULL (before the cast)
+ *  lse_out      fp32 [batch][num_heads] or NULL (merged LSE)
+ * At least one of out_bf16 / out_f32 must be non-NULL.  num_shards 1..64;
+ * head_dim_v a positive multiple of 32 up to 1024; out_dim a positive multiple
+ * of 16 up to 256; num_heads up to 65535.  partial_out and w_uv_t 16-byte
+ * aligned, the rest aligned to their element size.  A row whose partials are
+ * all empty gives y = 0 and lse* = -inf. */
+dcp_status dcp_combine_vproj_gate(int32_t num_shards, int32_t batch, int32_t num_heads, int32_t head_dim_v,
+                                  int32_t out_dim, const float* partial_out, const float* partial_lse,
+                                  const void* w_uv_t, const void* gate, void* out_bf16, float* out_f32,
+                                  float* lse_out, hipStream_t stream);
 
 /* ------------------------------------------------------------- helpers */
 

@@ -239,4 +239,33 @@ dcp_status dcp_combine(int32_t num_shards, int32_t batch, int32_t num_heads, int
   return hip_status(dcp::launch_combine(a, stream));
 }
 
+dcp_status dcp_combine_vproj_gate(int32_t num_shards, int32_t batch, int32_t num_heads, int32_t head_dim_v,
+                                  int32_t out_dim, const float* partial_out, const float* partial_lse,
+                                  const void* w_uv_t, const void* gate, void* out_bf16, float* out_f32,
+                                  float* lse_out, hipStream_t stream) {
+  if (num_shards < 1 || batch < 0 || num_heads < 1 || head_dim_v < 1 || out_dim < 1) return DCP_ERR_INVALID_ARGUMENT;
+  if (num_shards > 64 || head_dim_v % 32 != 0 || head_dim_v > 1024 || out_dim % 16 != 0 || out_dim > 256)
+    return DCP_ERR_UNSUPPORTED;
+  if ((int64_t)batch * num_heads > INT32_MAX / 4 || num_heads > 65535) return DCP_ERR_UNSUPPORTED;
+  if (batch == 0) return DCP_OK;
+  if (!partial_out || !partial_lse || !w_uv_t || (!out_bf16 && !out_f32)) return DCP_ERR_INVALID_ARGUMENT;
+  if (!aligned(partial_out, 16) || !aligned(partial_lse, 4) || !aligned(w_uv_t, 16) || !aligned(gate, 2) ||
+      !aligned(out_bf16, 2) || !aligned(out_f32, 4) || !aligned(lse_out, 4))
+    return DCP_ERR_INVALID_ARGUMENT;
+  dcp::VprojArgs a;
+  a.po = partial_out;
+  a.plse = partial_lse;
+  a.w = (const uint16_t*)w_uv_t;
+  a.gate = (const uint16_t*)gate;
+  a.out_bf16 = (uint16_t*)out_bf16;
+  a.out_f32 = out_f32;
+  a.lse_out = lse_out;
+  a.nshards = num_shards;
+  a.batch = batch;
+  a.heads = num_heads;
+  a.dv = head_dim_v;
+  a.dvo = out_dim;
+  return hip_status(dcp::launch_combine_vproj(a, stream));
+}
+
 }  // extern "C"

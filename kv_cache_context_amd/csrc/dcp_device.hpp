@@ -157,4 +157,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
+__device__ __forceinline__ uint16_t bf16_bits_rne(float a) {
+  const __bf16 x = (__bf16)a;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, x);
+}
+
 }  // namespace dcp

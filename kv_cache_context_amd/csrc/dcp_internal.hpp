@@ -73,8 +73,20 @@ struct CombineArgs {
   float pad;
 };
 
+struct VprojArgs {
+  const float* po;
+  const float* plse;
+  const uint16_t* w;     // bf16 [heads][dvo][dv]
+  const uint16_t* gate;  // bf16 [batch][heads][dvo] or null
+  uint16_t* out_bf16;
+  float* out_f32;
+  float* lse_out;
+  int nshards, batch, heads, dv, dvo;
+};
+
 hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_gqa_partial(const GqaArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_combine_vproj(const VprojArgs& a, hipStream_t stream);
 
 }  // namespace dcp

@@ -31,7 +31,7 @@ DCP_LAYOUT_CONTIGUOUS = 1
 EXPORTED = (
     "dcp_mla_workspace_bytes", "dcp_mla_decode_partial",
     "dcp_gqa_workspace_bytes", "dcp_gqa_decode_partial",
-    "dcp_combine", "dcp_status_string", "dcp_last_hip_error", "dcp_abi_version",
+    "dcp_combine", "dcp_combine_vproj_gate", "dcp_status_string", "dcp_last_hip_error", "dcp_abi_version",
 )
 
 
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.dcp_combine.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                               _P, _P, _P, _P, _P, _P]
     L.dcp_combine.restype = ctypes.c_int
+    L.dcp_combine_vproj_gate.argtypes = [ctypes.c_int32] * 5 + [_P] * 8
+    L.dcp_combine_vproj_gate.restype = ctypes.c_int
     L.dcp_status_string.argtypes = [ctypes.c_int]
     L.dcp_status_string.restype = ctypes.c_char_p
     L.dcp_last_hip_error.argtypes = []
@@ -143,6 +145,13 @@ def dcp_combine(num_shards: int, batch: int, num_heads: int, head_dim_v: int, pa
                 partial_lse: int, out_bf16: int, out_f32: int, lse_out: int, stream: int) -> int:
     return int(lib().dcp_combine(num_shards, batch, num_heads, head_dim_v, partial_out, partial_lse,
                                  out_bf16, out_f32, lse_out, stream))
+
+
+def dcp_combine_vproj_gate(num_shards: int, batch: int, num_heads: int, head_dim_v: int, out_dim: int,
+                           partial_out: int, partial_lse: int, w_uv_t: int, gate: int, out_bf16: int,
+                           out_f32: int, lse_out: int, stream: int) -> int:
+    return int(lib().dcp_combine_vproj_gate(num_shards, batch, num_heads, head_dim_v, out_dim, partial_out,
+                                            partial_lse, w_uv_t, gate, out_bf16, out_f32, lse_out, stream))
 
 
 def check(status: int, what: str = "") -> None:

@@ -128,3 +128,37 @@ def dcp_combine(partial_out, partial_lse, out_bf16=None, out_f32=None, lse_out=N
     ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
     _abi.check(_abi.dcp_combine(n, b, h, dv, partial_out.data_ptr(), partial_lse.data_ptr(), ptr(out_bf16),
                                 ptr(out_f32), ptr(lse_out), _stream(stream)), "dcp_combine")
+
+
+def dcp_combine_vproj_gate(partial_out, partial_lse, w_uv_t, gate=None, out_bf16=None, out_f32=None,
+                           lse_out=None, stream=None) -> None:
+    """Merge + per-head value up-projection + sigmoid gate (include/dcp.h).
+
+    partial_out fp32 [N, b, H, Dv], partial_lse fp32 [N, b, H], w_uv_t bf16
+    [H, Dvo, Dv], gate bf16 [b, H, Dvo] or None; outputs [b, H, Dvo]."""
+    _req(partial_out, torch.float32, 4, "partial_out")
+    _req(partial_lse, torch.float32, 3, "partial_lse")
+    _req(w_uv_t, torch.bfloat16, 3, "w_uv_t")
+    n, b, h, dv = partial_out.shape
+    if tuple(partial_lse.shape) != (n, b, h):
+        raise ValueError("partial_lse shape")
+    if w_uv_t.shape[0] != h or w_uv_t.shape[2] != dv:
+        raise ValueError("w_uv_t shape")
+    dvo = w_uv_t.shape[1]
+    if gate is not None:
+        _req(gate, torch.bfloat16, 3, "gate")
+        if tuple(gate.shape) != (b, h, dvo):
+            raise ValueError("gate shape")
+    for name, t, dt in (("out_bf16", out_bf16, torch.bfloat16), ("out_f32", out_f32, torch.float32)):
+        if t is not None:
+            _req(t, dt, 3, name)
+            if tuple(t.shape) != (b, h, dvo):
+                raise ValueError(f"{name} shape")
+    if lse_out is not None:
+        _req(lse_out, torch.float32, 2, "lse_out")
+        if tuple(lse_out.shape) != (b, h):
+            raise ValueError("lse_out shape")
+    ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+    _abi.check(_abi.dcp_combine_vproj_gate(n, b, h, dv, dvo, partial_out.data_ptr(), partial_lse.data_ptr(),
+                                           w_uv_t.data_ptr(), ptr(gate), ptr(out_bf16), ptr(out_f32),
+                                           ptr(lse_out), _stream(stream)), "dcp_combine_vproj_gate")

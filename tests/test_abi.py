@@ -107,6 +107,24 @@ def test_combine_validation():
     assert c(8, 0, 64, 512, 0, 0, 0, 0, 0, 0) == 0               # empty batch: no-op
 
 
+def test_combine_vproj_gate_validation():
+    c = dcp.dcp_combine_vproj_gate
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, 0)  # partials, lse, w, gate, out_bf16, out_f32, lse_out, stream
+    assert c(0, 1, 1, 512, 128, *ok) == 1
+    assert c(65, 1, 1, 512, 128, *ok) == 2
+    assert c(8, 1, 1, 500, 128, *ok) == 2           # latent width not a multiple of 32
+    assert c(8, 1, 1, 2048, 128, *ok) == 2
+    assert c(8, 1, 1, 512, 120, *ok) == 2           # output width not a multiple of 16
+    assert c(8, 1, 1, 512, 272, *ok) == 2
+    assert c(8, 1, 1, 512, 0, *ok) == 1
+    assert c(8, 1, 70000, 512, 128, *ok) == 2
+    assert c(8, 1, 1, 512, 128, FAKE, FAKE, 0, FAKE, FAKE, 0, 0, 0) == 1       # no projection
+    assert c(8, 1, 1, 512, 128, FAKE, FAKE, FAKE, FAKE, 0, 0, 0, 0) == 1       # no output at all
+    assert c(8, 1, 1, 512, 128, FAKE, FAKE, FAKE + 8, FAKE, FAKE, 0, 0, 0) == 1  # misaligned projection
+    assert c(8, 1, 1, 512, 128, FAKE, FAKE, FAKE, FAKE + 1, FAKE, 0, 0, 0) == 1  # misaligned gate
+    assert c(8, 0, 64, 512, 128, 0, 0, 0, 0, 0, 0, 0, 0) == 0                  # empty batch: no-op
+
+
 def test_ops_reject_cpu_tensors():
     import torch
     p = mla(batch=1)
