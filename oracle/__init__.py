@@ -20,6 +20,9 @@ Every function follows a stated definition:
   (section 5.4 "GQA Backend").
 * ``shard_positions`` — which global token positions a shard holds
   (section 4; round-robin and contiguous layouts).
+* ``query_limit`` / ``query_positions`` — the causal prefix of each query
+  token of a multi-token decode step (speculative verification, section 6) and
+  the part of it a shard holds.
 * ``merge`` — the LSE-weighted merge of N partial results into the exact
   output (section 4.1, the AllGather + ReduceScatter step, which reweights
   partial outputs by their LSE values).
@@ -38,6 +41,8 @@ from .attention import (  # noqa: F401
     mla_attention,
     gqa_attention,
     shard_positions,
+    query_limit,
+    query_positions,
     mla_shard_partial,
     gqa_shard_partial,
     merge,

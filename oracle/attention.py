@@ -97,6 +97,23 @@ def shard_positions(L: int, n: int, r: int, layout: int = ROUND_ROBIN) -> np.nda
     return t[(t >= r * c) & (t < (r + 1) * c)]
 
 
+def query_limit(L: int, q_len: int, j: int) -> int:
+    """Number of leading cache positions query token j of a q_len-token decode
+    step attends (multi-token decode for speculative verification, DCP post
+    section 6 "Future Work"): the cache holds L positions whose last q_len are
+    the step's own tokens, and token j sees the positions before it and itself,
+    i.e. t <= L - q_len + j.  Clamped at 0."""
+    return max(0, L - q_len + 1 + j)
+
+
+def query_positions(L: int, q_len: int, j: int, n: int, r: int, layout: int = ROUND_ROBIN) -> np.ndarray:
+    """Shard r's positions attended by query token j: the shard's part of the
+    cache of length L (the sharding is a property of the cache, so the
+    contiguous layout cuts by ceil(L / n)) below query j's causal limit."""
+    t = shard_positions(L, n, r, layout)
+    return t[t < query_limit(L, q_len, j)]
+
+
 def mla_shard_partial(q, kv_full, scale, n, r, layout=ROUND_ROBIN, kv_lora_rank=512):
     """Shard r's partial (o, lse): MLA attention over its local slice only."""
     idx = shard_positions(kv_full.shape[0], n, r, layout)

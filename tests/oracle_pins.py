@@ -394,4 +394,42 @@ def pin_vproj_torch(impl):
     _close(y, ref, tol=1e-11, what="vproj vs torch")
 
 
+def pin_query_positions(impl):
+    """Multi-token steps: for every query token, the shards' attended positions
+    are disjoint and together are exactly the causal prefix 0 .. L - q_len + j
+    (enumerated by brute force), for both layouts; q_len = 1 is the whole cache."""
+    for L in (1, 2, 5, 17, 64, 100):
+        for n in (1, 2, 3, 8):
+            for layout in (0, 1):
+                assert np.array_equal(np.sort(np.concatenate([impl.query_positions(L, 1, 0, n, r, layout)
+                                                              for r in range(n)])), np.arange(L))
+                for q_len in (2, 3, 9):
+                    for j in range(q_len):
+                        want = [t for t in range(L) if t <= L - q_len + j]
+                        parts = [impl.query_positions(L, q_len, j, n, r, layout) for r in range(n)]
+                        got = np.sort(np.concatenate(parts))
+                        assert got.tolist() == want, (L, n, layout, q_len, j)
+                        assert sum(len(p) for p in parts) == len(want)
+                        # and each shard's part lies inside that shard's slice of the cache
+                        for r in range(n):
+                            assert set(parts[r].tolist()) <= set(impl.shard_positions(L, n, r, layout).tolist())
+
+
+def pin_query_merge(impl):
+    """Merging the shards' per-query partials gives attention over that query's
+    causal prefix, for each query token of a 3-token step."""
+    r_ = _rng(44)
+    q, kv = _mla_case(r_, 3, 29)
+    L, q_len, n = 29, 3, 4
+    for layout in (0, 1):
+        for j in range(q_len):
+            lim = impl.query_limit(L, q_len, j)
+            o_ref, lse_ref = impl.mla_attention(q, kv[:lim], 0.4, 24)
+            parts = [impl.mla_attention(q, kv[impl.query_positions(L, q_len, j, n, r, layout)], 0.4, 24)
+                     for r in range(n)]
+            o, lse = impl.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+            _close(o, o_ref, what="query merge o")
+            _close(lse, lse_ref, what="query merge lse")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

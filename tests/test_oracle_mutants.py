@@ -45,6 +45,10 @@ MUTANTS = {
     "vproj wrong head": ("y[:, h, :] = o[:, h, :] @ w[h].T", "y[:, h, :] = o[:, h, :] @ w[(h + 1) % w.shape[0]].T"),
     "gate sign": ("sig = 1.0 / (1.0 + np.exp(-g))", "sig = 1.0 / (1.0 + np.exp(g))"),
     "gate missing": ("return sig * y, lse", "return y, lse"),
+    "query limit excludes itself": ("return max(0, L - q_len + 1 + j)", "return max(0, L - q_len + j)"),
+    "query limit from the front": ("return max(0, L - q_len + 1 + j)", "return max(0, min(L, q_len + j))"),
+    "query positions re-sharded by prefix": ("    t = shard_positions(L, n, r, layout)\n    return t[t < query_limit(L, q_len, j)]",
+                                            "    return shard_positions(query_limit(L, q_len, j), n, r, layout)"),
 }
 
 
