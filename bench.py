@@ -56,8 +56,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(case, r):
-    """Bytes the method must move for shard r's partial (KV once, q, outputs, tables)."""
+def algorithmic_bytes(case, r, q_len=1):
+    """Bytes the method must move for shard r's partial: the shard's KV once
+    (a q_len-token step's tokens share it), q, outputs and tables."""
     w = case.w
     ll = case.local_lens(r)
     nblk = -(-ll // w.block_size)
@@ -65,34 +66,44 @@ def algorithmic_bytes(case, r):
         kv = int(ll.sum()) * w.dk * 2
     else:
         kv = int(ll.sum()) * w.kv_heads * w.head_dim * 2 * 2
-    q = w.batch * w.heads * w.dk * 2
-    out = w.batch * w.heads * (w.dv + 1) * 4
+    q = w.batch * q_len * w.heads * w.dk * 2
+    out = w.batch * q_len * w.heads * (w.dv + 1) * 4
     meta = int(nblk.sum()) * 4 + w.batch * 4
     return kv + q + out + meta, kv
 
 
-def algorithmic_flops(case, r):
+def attended(case, r, q_len):
+    """(request, token) pairs' attended positions on shard r, summed."""
+    import oracle
     w = case.w
-    ll = int(case.local_lens(r).sum())
+    if q_len == 1:
+        return int(case.local_lens(r).sum())
+    return sum(len(oracle.query_positions(int(L), q_len, j, w.num_shards, r, w.layout))
+               for L in case.seq_lens for j in range(q_len))
+
+
+def algorithmic_flops(case, r, q_len=1):
+    w = case.w
+    ll = attended(case, r, q_len)
     if w.kind == "mla":
         return ll * w.heads * 2 * (w.dk + w.dv)
     return ll * w.heads * 4 * w.head_dim
 
 
-def combine_bytes(w):
-    return w.num_shards * w.batch * w.heads * (w.dv + 1) * 4 + w.batch * w.heads * w.dv * 2
+def combine_bytes(w, q_len=1):
+    return (w.num_shards * w.batch * w.heads * (w.dv + 1) * 4 + w.batch * w.heads * w.dv * 2) * q_len
 
 
 VPROJ_DVO = 128  # projected head width of the fused epilogue
 
 
-def vproj_bytes(w):
+def vproj_bytes(w, q_len=1):
     """Fused combine epilogue: partials + LSEs in, projection weights, gate logits, bf16 out."""
-    return (w.num_shards * w.batch * w.heads * (w.dv + 1) * 4 + w.heads * VPROJ_DVO * w.dv * 2
-            + 2 * w.batch * w.heads * VPROJ_DVO * 2)
+    return (q_len * w.num_shards * w.batch * w.heads * (w.dv + 1) * 4 + w.heads * VPROJ_DVO * w.dv * 2
+            + 2 * q_len * w.batch * w.heads * VPROJ_DVO * 2)
 
 
-def cpu_baseline(case, budget_s=10.0):
+def cpu_baseline(case, budget_s=10.0, q_len=1):
     """The fp64 oracle on the host cores, on a bounded sample of the same step.
 
     The oracle computes the timed shards' partials request by request (its own
@@ -105,7 +116,8 @@ def cpu_baseline(case, budget_s=10.0):
     import oracle
     w = case.w
     ranks = list(w.ranks)
-    total_tokens = sum(int(case.local_lens(r).sum()) for r in ranks)
+    total_tokens = sum(attended(case, r, q_len) for r in ranks)
+    qs = case.queries(q_len) if q_len > 1 else case.q[:, None]
     done_tokens = 0
     t_spent = 0.0
     reqs = 0
@@ -115,29 +127,34 @@ def cpu_baseline(case, budget_s=10.0):
         if b not in cache:
             if len(cache) > 4:
                 cache.pop(next(iter(cache)))
-            q = oracle.widen_bf16(case.q[b])
+            L = int(case.seq_lens[b])
             shard_in = []
             for r in range(w.num_shards):
-                pos = oracle.shard_positions(int(case.seq_lens[b]), w.num_shards, r, w.layout)
+                pos = oracle.shard_positions(L, w.num_shards, r, w.layout)
                 if r in ranks:
                     rows = case.rows_at(b, pos)
-                    shard_in.append((r, len(pos), [oracle.widen_bf16(x) for x in rows]))
+                    shard_in.append((r, pos, [oracle.widen_bf16(x) for x in rows]))
                 else:
-                    shard_in.append((r, len(pos), None))
-            cache[b] = (q, shard_in)
-        q, shard_in = cache[b]
+                    shard_in.append((r, pos, None))
+            cache[b] = ([oracle.widen_bf16(qs[b, j]) for j in range(q_len)], shard_in)
+        qj, shard_in = cache[b]
+        L = int(case.seq_lens[b])
         t0 = time.perf_counter()
-        parts = []
-        for r, npos, rows in shard_in:
-            if rows is None:
-                parts.append((np.zeros((w.heads, w.dv)), np.full(w.heads, -np.inf)))
-            elif w.kind == "mla":
-                parts.append(oracle.mla_attention(q, rows[0], w.scale, w.kv_lora_rank))
-            else:
-                parts.append(oracle.gqa_attention(q, rows[0], rows[1], w.scale))
-        oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+        for j in range(q_len):
+            lim = oracle.query_limit(L, q_len, j)
+            parts = []
+            for r, pos, rows in shard_in:
+                m = int(np.searchsorted(pos, lim))  # shard positions below token j's limit
+                if rows is None:
+                    parts.append((np.zeros((w.heads, w.dv)), np.full(w.heads, -np.inf)))
+                elif w.kind == "mla":
+                    parts.append(oracle.mla_attention(qj[j], rows[0][:m], w.scale, w.kv_lora_rank))
+                else:
+                    parts.append(oracle.gqa_attention(qj[j], rows[0][:m], rows[1][:m], w.scale))
+                if rows is not None:
+                    done_tokens += m
+            oracle.merge(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
         t_spent += time.perf_counter() - t0
-        done_tokens += sum(npos for r, npos, rows in shard_in if rows is not None)
         reqs += 1
         b = (b + 1) % w.batch
     frac = done_tokens / max(total_tokens, 1)
@@ -148,7 +165,8 @@ def cpu_baseline(case, budget_s=10.0):
         cores = os.cpu_count()
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {"value": round(us_per_step, 1), "unit": "us/step", "cores": min(cores, threads), "kind": "oracle",
-            "sample": f"{reqs} request-steps of the {w.batch}-request step ({frac:.2f} steps' worth of local "
+            "sample": f"{reqs} request-steps ({q_len} query token(s) each) of the {w.batch}-request step "
+                      f"({frac:.2f} steps' worth of local "
                       f"tokens), fp64 numpy, {t_spent:.1f} s of oracle time, scaled to one step"}
 
 
@@ -163,6 +181,8 @@ def main():
     ap.add_argument("--epilogue", choices=("combine", "vproj"), default="combine",
                     help="step epilogue: LSE combine + bf16 cast, or the combine fused with the per-head value "
                          "up-projection (128 wide) and sigmoid gate (MLA workloads)")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per request (multi-token decode step, causal within the step)")
     ap.add_argument("--warm-cache", action="store_true", help="no KV rotation (reported as such)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
@@ -179,6 +199,11 @@ def main():
     from kv_cache_context_amd import ops
 
     w = W.WORKLOADS[args.workload]
+    ql = args.q_len
+    if not 1 <= ql <= 16:
+        print(json.dumps({"error": "--q-len must be in 1..16"}))
+        sys.exit(2)
+    rows = w.batch * ql
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     case = W.Case(w, seed=args.seed)
@@ -187,9 +212,9 @@ def main():
     hint = max(1, case.max_seq_len)
     log(f"[bench] workload {w.name}: {w.description}; seq_lens total {int(case.seq_lens.sum())}")
 
-    po = torch.empty((n, w.batch, w.heads, w.dv), dtype=torch.float32, device=dev)
-    pl = torch.empty((n, w.batch, w.heads), dtype=torch.float32, device=dev)
-    q_d = bf16_tensor(case.q, dev)
+    po = torch.empty((n, rows, w.heads, w.dv), dtype=torch.float32, device=dev)
+    pl = torch.empty((n, rows, w.heads), dtype=torch.float32, device=dev)
+    q_d = bf16_tensor(case.queries(ql).reshape(rows, w.heads, w.dk) if ql > 1 else case.q, dev)
     lens_d = int32_tensor(case.seq_lens, dev)
     shards = {}
     t0 = time.time()
@@ -198,7 +223,7 @@ def main():
         sc = caches[r]
         caches[r] = None
         common = dict(block_size=w.block_size, max_blocks_per_seq=mb, num_blocks=sc.num_blocks, shard_rank=r,
-                      num_shards=n, layout=w.layout, max_seq_len_hint=hint, softmax_scale=w.scale)
+                      num_shards=n, layout=w.layout, max_seq_len_hint=hint, softmax_scale=w.scale, q_len=ql)
         ent = {"table": int32_tensor(sc.block_table, dev)}
         if w.kind == "mla":
             ent["p"] = ops.mla_params(batch=w.batch, num_heads=w.heads, **common)
@@ -241,7 +266,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {copies} rotating copies of the timed KV ({kv_bytes_timed / 1e6:.1f} MB each)")
 
-    out_bf = torch.empty((w.batch, w.heads, w.dv), dtype=torch.bfloat16, device=dev)
+    out_bf = torch.empty((rows, w.heads, w.dv), dtype=torch.bfloat16, device=dev)
 
     def do_partials(i):
         for r in timed:
@@ -251,9 +276,9 @@ def main():
         if w.kind != "mla":
             print(json.dumps({"error": "--epilogue vproj applies to the MLA workloads"}))
             sys.exit(2)
-        w_bits, g_bits = W.random_vproj(w.batch, w.heads, VPROJ_DVO, w.dv, seed=args.seed)
+        w_bits, g_bits = W.random_vproj(rows, w.heads, VPROJ_DVO, w.dv, seed=args.seed)
         w_uv_d, gate_d = bf16_tensor(w_bits, dev), bf16_tensor(g_bits, dev)
-        out_bf = torch.empty((w.batch, w.heads, VPROJ_DVO), dtype=torch.bfloat16, device=dev)
+        out_bf = torch.empty((rows, w.heads, VPROJ_DVO), dtype=torch.bfloat16, device=dev)
 
     def do_combine(i):
         if args.epilogue == "vproj":
@@ -310,9 +335,9 @@ def main():
     part_mean = part_ms / args.steps * 1e3
     comb_mean = comb_ms / args.steps * 1e3
 
-    alg_partial = sum(algorithmic_bytes(case, r)[0] for r in timed)
-    alg_comb = vproj_bytes(w) if args.epilogue == "vproj" else combine_bytes(w)
-    flops = sum(algorithmic_flops(case, r) for r in timed)
+    alg_partial = sum(algorithmic_bytes(case, r, ql)[0] for r in timed)
+    alg_comb = vproj_bytes(w, ql) if args.epilogue == "vproj" else combine_bytes(w, ql)
+    flops = sum(algorithmic_flops(case, r, ql) for r in timed)
     achieved = alg_partial / (part_mean * 1e-6) / 1e9
     step_gbs = (alg_partial + alg_comb) / (ms_per_step * 1e-3) / 1e9
 
@@ -330,7 +355,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "kind": w.kind, "batch": w.batch,
-                   "heads": w.heads, "num_shards": n, "timed_shards": timed, "block_size": w.block_size,
+                   "heads": w.heads, "q_len": ql, "num_shards": n, "timed_shards": timed, "block_size": w.block_size,
                    "local_tokens": int(sum(case.local_lens(r).sum() for r in timed)),
                    "kv_copies_rotated": copies},
         "step_hbm_gbps": round(step_gbs, 1),
@@ -354,10 +379,10 @@ def main():
         torch.cuda.synchronize()
         del a, b2
     kind = "mla" if w.kind == "mla" else "gqa"
-    res["roofline"]["traffic"] = stored_traffic(kind, w.name)
+    res["roofline"]["traffic"] = stored_traffic(kind, w.name) if ql == 1 else None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")
-        res["cpu_baseline"] = cpu_baseline(case)
+        res["cpu_baseline"] = cpu_baseline(case, q_len=ql)
     print(json.dumps(res), flush=True)
 
 

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define DCP_ABI_VERSION 1
+#define DCP_ABI_VERSION 2
 
 typedef enum {
   DCP_OK = 0,
@@ -76,6 +76,19 @@ typedef enum {
  * length L, N, r and the layout. */
 typedef enum { DCP_LAYOUT_ROUND_ROBIN = 0, DCP_LAYOUT_CONTIGUOUS = 1 } dcp_layout;
 
+/* Multi-token steps (q_len = Q > 1), for verifying Q speculative tokens in one
+ * decode step (DCP post, section 6 "Future Work", names MTP / speculative
+ * decoding with DCP): the cache already holds the step's Q tokens as its last
+ * Q positions, seq_lens[b] = L counts them, and query token j (0-based) of
+ * request b attends the causal prefix of global positions t <= L - Q + j.
+ * The shard layout is that of the cache of length L (for CONTIGUOUS,
+ * C = ceil(L/N)); each shard attends the part of every query's prefix it
+ * holds.  q, out and lse gain a token index after the request index:
+ *     q [batch][Q][heads][dk], out [batch][Q][heads][dv], lse [batch][Q][heads]
+ * block_table and seq_lens stay per request.  batch * Q <= 2048.  Each (request,
+ * token) pair is its own row set in the split (the KV slice is read once per
+ * query token). */
+
 /* ------------------------------------------------------------------ MLA */
 
 typedef struct {
@@ -92,6 +105,8 @@ typedef struct {
   int32_t max_seq_len_hint;   /* host-known upper bound on seq_lens[]; >= 1; the shard's
                                  local slice of such a request must fit in one table row     */
   float softmax_scale;        /* multiplies <q, k> before the softmax (> 0, finite)         */
+  int32_t q_len;              /* query tokens per request in this step, 0..16 (0 means 1);
+                                 see "Multi-token steps" below                               */
 } dcp_mla_params;
 
 /* Bytes of device workspace dcp_mla_decode_partial needs for `p`
@@ -137,6 +152,7 @@ typedef struct {
   dcp_layout layout;
   int32_t max_seq_len_hint;
   float softmax_scale;
+  int32_t q_len;              /* as in dcp_mla_params                                       */
 } dcp_gqa_params;
 
 size_t dcp_gqa_workspace_bytes(const dcp_gqa_params* p);

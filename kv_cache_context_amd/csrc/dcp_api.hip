@@ -86,17 +86,31 @@ dcp::SplitArgs split_args(int batch, int block_size, int max_blocks, int num_blo
   s.G = 0;
   s.min_tiles = 1;
   s.seg_cost = 0;
+  s.q_len = 1;
   s.scale = scale;
   s.c = scale * 1.4426950408889634f;
   return s;
 }
 
+// Query tokens per request (0 means 1) and the row sets of the split.
+int qlen_of(int32_t q_len) { return q_len <= 0 ? 1 : q_len; }
+int rows_of(int32_t batch, int32_t q_len) {
+  const int64_t r = (int64_t)batch * qlen_of(q_len);
+  return r > INT32_MAX ? INT32_MAX : (int)r;
+}
+dcp_status check_qlen(int32_t q_len) {
+  if (q_len < 0) return DCP_ERR_INVALID_ARGUMENT;
+  if (q_len > 16) return DCP_ERR_UNSUPPORTED;
+  return DCP_OK;
+}
+
 dcp_status mla_check(const dcp_mla_params* p) {
   if (!p) return DCP_ERR_INVALID_ARGUMENT;
+  if (check_qlen(p->q_len) != DCP_OK) return check_qlen(p->q_len);
   if (p->num_heads < 1 || p->kv_lora_rank < 1 || p->rope_dim < 1) return DCP_ERR_INVALID_ARGUMENT;
-  dcp_status st = check_split(p->batch, p->block_size, p->max_blocks_per_seq, p->num_blocks,
-                              p->shard_rank, p->num_shards, p->layout, p->max_seq_len_hint,
-                              p->softmax_scale);
+  dcp_status st = check_split(p->batch < 0 ? -1 : rows_of(p->batch, p->q_len), p->block_size,
+                              p->max_blocks_per_seq, p->num_blocks, p->shard_rank, p->num_shards, p->layout,
+                              p->max_seq_len_hint, p->softmax_scale);
   if (st != DCP_OK) return st;
   if (p->kv_lora_rank != 512 || p->rope_dim != 64) return DCP_ERR_UNSUPPORTED;
   if (p->num_heads % 16 != 0 || p->num_heads > 64) return DCP_ERR_UNSUPPORTED;
@@ -105,11 +119,12 @@ dcp_status mla_check(const dcp_mla_params* p) {
 
 dcp_status gqa_check(const dcp_gqa_params* p) {
   if (!p) return DCP_ERR_INVALID_ARGUMENT;
+  if (check_qlen(p->q_len) != DCP_OK) return check_qlen(p->q_len);
   if (p->num_q_heads < 1 || p->num_kv_heads < 1 || p->head_dim < 1) return DCP_ERR_INVALID_ARGUMENT;
   if (p->num_q_heads % p->num_kv_heads != 0) return DCP_ERR_INVALID_ARGUMENT;
-  dcp_status st = check_split(p->batch, p->block_size, p->max_blocks_per_seq, p->num_blocks,
-                              p->shard_rank, p->num_shards, p->layout, p->max_seq_len_hint,
-                              p->softmax_scale);
+  dcp_status st = check_split(p->batch < 0 ? -1 : rows_of(p->batch, p->q_len), p->block_size,
+                              p->max_blocks_per_seq, p->num_blocks, p->shard_rank, p->num_shards, p->layout,
+                              p->max_seq_len_hint, p->softmax_scale);
   if (st != DCP_OK) return st;
   if (p->head_dim != 128) return DCP_ERR_UNSUPPORTED;
   if (p->num_kv_heads % 4 != 0 || p->num_kv_heads > 64) return DCP_ERR_UNSUPPORTED;
@@ -138,7 +153,7 @@ const char* dcp_status_string(dcp_status s) {
 
 size_t dcp_mla_workspace_bytes(const dcp_mla_params* p) {
   if (mla_check(p) != DCP_OK) return 0;
-  return dcp::ws_layout(p->batch, p->num_heads, 512).total;
+  return dcp::ws_layout(rows_of(p->batch, p->q_len), p->num_heads, 512).total;
 }
 
 dcp_status dcp_mla_decode_partial(const dcp_mla_params* p, const void* q, const void* kv_cache,
@@ -152,16 +167,18 @@ dcp_status dcp_mla_decode_partial(const dcp_mla_params* p, const void* q, const 
   if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
       !aligned(seq_lens, 4) || !aligned(lse, 4))
     return DCP_ERR_INVALID_ARGUMENT;
-  const dcp::WsLayout wl = dcp::ws_layout(p->batch, p->num_heads, 512);
+  const int rows = rows_of(p->batch, p->q_len);
+  const dcp::WsLayout wl = dcp::ws_layout(rows, p->num_heads, 512);
   if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
   hipError_t herr = hipSuccess;
   const int cus = device_cus(&herr);
   if (cus <= 0) return hip_status(herr);
 
   dcp::MlaArgs a;
-  a.s = split_args(p->batch, p->block_size, p->max_blocks_per_seq, p->num_blocks, p->shard_rank,
+  a.s = split_args(rows, p->block_size, p->max_blocks_per_seq, p->num_blocks, p->shard_rank,
                    p->num_shards, p->layout, p->softmax_scale, block_table, seq_lens, out, lse,
                    workspace, wl);
+  a.s.q_len = qlen_of(p->q_len);
   a.s.G = env_int("DCP_SPLIT_WGS", cus < dcp::kMaxSplitWGs ? cus : dcp::kMaxSplitWGs, 1,
                   dcp::kMaxSplitWGs);
   a.s.min_tiles = env_int("DCP_MLA_MIN_TILES", 4, 1, 1 << 20);
@@ -174,7 +191,7 @@ dcp_status dcp_mla_decode_partial(const dcp_mla_params* p, const void* q, const 
 
 size_t dcp_gqa_workspace_bytes(const dcp_gqa_params* p) {
   if (gqa_check(p) != DCP_OK) return 0;
-  return dcp::ws_layout(p->batch, p->num_q_heads, 128).total;
+  return dcp::ws_layout(rows_of(p->batch, p->q_len), p->num_q_heads, 128).total;
 }
 
 dcp_status dcp_gqa_decode_partial(const dcp_gqa_params* p, const void* q, const void* k_cache,
@@ -189,16 +206,18 @@ dcp_status dcp_gqa_decode_partial(const dcp_gqa_params* p, const void* q, const 
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(lse, 4))
     return DCP_ERR_INVALID_ARGUMENT;
-  const dcp::WsLayout wl = dcp::ws_layout(p->batch, p->num_q_heads, 128);
+  const int rows = rows_of(p->batch, p->q_len);
+  const dcp::WsLayout wl = dcp::ws_layout(rows, p->num_q_heads, 128);
   if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
   hipError_t herr = hipSuccess;
   const int cus = device_cus(&herr);
   if (cus <= 0) return hip_status(herr);
 
   dcp::GqaArgs a;
-  a.s = split_args(p->batch, p->block_size, p->max_blocks_per_seq, p->num_blocks, p->shard_rank,
+  a.s = split_args(rows, p->block_size, p->max_blocks_per_seq, p->num_blocks, p->shard_rank,
                    p->num_shards, p->layout, p->softmax_scale, block_table, seq_lens, out, lse,
                    workspace, wl);
+  a.s.q_len = qlen_of(p->q_len);
   // one workgroup column per group of 4 KV heads; together they fill the chip once
   const int groups = p->num_kv_heads / 4;
   int g = (cus + groups - 1) / groups;

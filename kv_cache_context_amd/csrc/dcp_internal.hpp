@@ -44,6 +44,7 @@ struct SplitArgs {
   int G;          // split workgroups launched
   int min_tiles;  // fewest tiles a split workgroup is given
   int seg_cost;   // tiles' worth of work charged for starting a request's segment
+  int q_len;      // query tokens per request: row set b is request b / q_len, token b % q_len
   float scale;    // softmax scale
   float c;        // softmax scale * log2(e)
 };

@@ -17,14 +17,35 @@
 
 namespace dcp {
 
-__device__ __forceinline__ int clamp_len(const SplitArgs& s, int L) {
-  const int lr = local_len(L, s.nshards, s.rank, s.layout);
+// Local length attended by row set b: request b / q_len, query token j =
+// b % q_len, whose causal prefix is the first L - q_len + 1 + j of the
+// request's L global positions.  The shard's part of the cache is cut from the
+// full length L (for the contiguous layout, runs of ceil(L / N)); the result is
+// capped at what one table row can address.
+__device__ __forceinline__ int clamp_len(const SplitArgs& s, int L, int j) {
+  int lr;
+  if (s.q_len <= 1 || s.layout == 0) {
+    lr = local_len(s.q_len <= 1 ? L : L - s.q_len + 1 + j, s.nshards, s.rank, s.layout);
+  } else {
+    const int lim = L - s.q_len + 1 + j;  // positions below lim are attended
+    const int64_t c = ((int64_t)(L > 0 ? L : 0) + s.nshards - 1) / s.nshards;
+    const int64_t lo = c * s.rank;
+    int64_t hi = lo + c;
+    if (hi > L) hi = L;
+    if (hi > lim) hi = lim;
+    lr = hi > lo ? (int)(hi - lo) : 0;
+  }
   const int cap = s.max_blocks * s.block_size;  // what one table row can address
   return lr < cap ? lr : cap;
 }
-// Local length of request b (b wave-uniform).
+// Local length of row set b (b wave-uniform).
 __device__ __forceinline__ int clamped_local_len(const SplitArgs& s, int b) {
-  return uni(clamp_len(s, ld_uniform(s.seq_lens, b)));
+  const int req = b / s.q_len;
+  return uni(clamp_len(s, ld_uniform(s.seq_lens, req), b - req * s.q_len));
+}
+// Block-table row of row set b.
+__device__ __forceinline__ const int32_t* table_row(const SplitArgs& s, int b) {
+  return s.table + (int64_t)(b / s.q_len) * s.max_blocks;
 }
 
 // Fills s_pref[0..batch] with the inclusive prefix sums of the requests' work
@@ -41,7 +62,10 @@ __device__ int plan_tiles(const SplitArgs& s, int tile, int* s_pref, int* s_wsum
   for (int base = 0; base < s.batch; base += THREADS) {
     const int b = base + tid;
     int n = 0;
-    if (b < s.batch) n = (clamp_len(s, s.seq_lens[b]) + tile - 1) / tile;
+    if (b < s.batch) {
+      const int req = b / s.q_len;
+      n = (clamp_len(s, s.seq_lens[req], b - req * s.q_len) + tile - 1) / tile;
+    }
     if (n > 0) n += s.seg_cost;
     int v = n;
 #pragma unroll

@@ -200,7 +200,7 @@ __device__ __forceinline__ void run_segment(const GqaArgs& a, Smem& sm, int quad
   DCP_LDS char* tiles = (DCP_LDS char*)sm.tiles;
   const int n = t1 - t0;
   const int lr = uni(clamped_local_len(s, b));
-  const int32_t* trow = s.table + (int64_t)b * s.max_blocks;
+  const int32_t* trow = table_row(s, b);
 
   // lane offsets of the copies: token 4*j + wave of the tile, chunk `lane` of its
   // 1 KiB (4 heads x 16 chunks), chunk index swizzled per token

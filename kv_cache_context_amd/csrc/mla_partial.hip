@@ -354,7 +354,7 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
   const float thr = 64.f / s.c;  // raw-score headroom of the fixed reference (p < 2^64)
   const int n = t1 - t0;
   const int lr = uni(clamped_local_len(s, b));
-  const int32_t* trow = s.table + (int64_t)b * s.max_blocks;
+  const int32_t* trow = table_row(s, b);
 
   // per-thread copy pattern of a tile: LDS chunk slot -> source chunk (swizzled)
   int goff[DMA_N], grow[DMA_N];

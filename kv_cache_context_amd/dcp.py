@@ -43,6 +43,7 @@ class dcp_mla_params(ctypes.Structure):
         ("num_blocks", ctypes.c_int32), ("shard_rank", ctypes.c_int32),
         ("num_shards", ctypes.c_int32), ("layout", ctypes.c_int32),
         ("max_seq_len_hint", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("q_len", ctypes.c_int32),
     ]
 
 
@@ -54,6 +55,7 @@ class dcp_gqa_params(ctypes.Structure):
         ("num_blocks", ctypes.c_int32), ("shard_rank", ctypes.c_int32),
         ("num_shards", ctypes.c_int32), ("layout", ctypes.c_int32),
         ("max_seq_len_hint", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("q_len", ctypes.c_int32),
     ]
 
 

@@ -33,15 +33,22 @@ def _req(t: torch.Tensor, dtype, ndim: int, name: str):
 
 
 def mla_params(*, batch, num_heads, block_size, max_blocks_per_seq, num_blocks, shard_rank, num_shards,
-               layout, max_seq_len_hint, softmax_scale, kv_lora_rank=512, rope_dim=64) -> _abi.dcp_mla_params:
+               layout, max_seq_len_hint, softmax_scale, kv_lora_rank=512, rope_dim=64,
+               q_len=1) -> _abi.dcp_mla_params:
     return _abi.dcp_mla_params(batch, num_heads, kv_lora_rank, rope_dim, block_size, max_blocks_per_seq,
-                               num_blocks, shard_rank, num_shards, layout, max_seq_len_hint, softmax_scale)
+                               num_blocks, shard_rank, num_shards, layout, max_seq_len_hint, softmax_scale, q_len)
 
 
 def gqa_params(*, batch, num_q_heads, num_kv_heads, block_size, max_blocks_per_seq, num_blocks, shard_rank,
-               num_shards, layout, max_seq_len_hint, softmax_scale, head_dim=128) -> _abi.dcp_gqa_params:
+               num_shards, layout, max_seq_len_hint, softmax_scale, head_dim=128, q_len=1) -> _abi.dcp_gqa_params:
     return _abi.dcp_gqa_params(batch, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
-                               num_blocks, shard_rank, num_shards, layout, max_seq_len_hint, softmax_scale)
+                               num_blocks, shard_rank, num_shards, layout, max_seq_len_hint, softmax_scale, q_len)
+
+
+def _rows(p) -> int:
+    """Row sets of a step: requests times query tokens (q, out and lse are
+    [batch * q_len, heads, ...], request-major)."""
+    return p.batch * max(1, p.q_len)
 
 
 def mla_workspace(p: _abi.dcp_mla_params, device) -> torch.Tensor:
@@ -66,15 +73,15 @@ def dcp_mla_decode_partial(p, q, kv_cache, block_table, seq_lens, out, lse, work
     _req(out, torch.float32, 3, "out")
     _req(lse, torch.float32, 2, "lse")
     dk = p.kv_lora_rank + p.rope_dim
-    if tuple(q.shape) != (p.batch, p.num_heads, dk):
-        raise ValueError(f"q shape {tuple(q.shape)} != {(p.batch, p.num_heads, dk)}")
+    if tuple(q.shape) != (_rows(p), p.num_heads, dk):
+        raise ValueError(f"q shape {tuple(q.shape)} != {(_rows(p), p.num_heads, dk)}")
     if tuple(kv_cache.shape) != (p.num_blocks, p.block_size, dk):
         raise ValueError(f"kv_cache shape {tuple(kv_cache.shape)} != {(p.num_blocks, p.block_size, dk)}")
     if tuple(block_table.shape) != (p.batch, p.max_blocks_per_seq):
         raise ValueError(f"block_table shape {tuple(block_table.shape)}")
     if tuple(seq_lens.shape) != (p.batch,):
         raise ValueError("seq_lens shape")
-    if tuple(out.shape) != (p.batch, p.num_heads, p.kv_lora_rank) or tuple(lse.shape) != (p.batch, p.num_heads):
+    if tuple(out.shape) != (_rows(p), p.num_heads, p.kv_lora_rank) or tuple(lse.shape) != (_rows(p), p.num_heads):
         raise ValueError("out/lse shape")
     _abi.check(_abi.dcp_mla_decode_partial(p, q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
                                            seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(),
@@ -91,14 +98,14 @@ def dcp_gqa_decode_partial(p, q, k_cache, v_cache, block_table, seq_lens, out, l
     _req(seq_lens, torch.int32, 1, "seq_lens")
     _req(out, torch.float32, 3, "out")
     _req(lse, torch.float32, 2, "lse")
-    if tuple(q.shape) != (p.batch, p.num_q_heads, p.head_dim):
+    if tuple(q.shape) != (_rows(p), p.num_q_heads, p.head_dim):
         raise ValueError("q shape")
     kshape = (p.num_blocks, p.block_size, p.num_kv_heads, p.head_dim)
     if tuple(k_cache.shape) != kshape or tuple(v_cache.shape) != kshape:
         raise ValueError(f"k/v cache shape must be {kshape}")
     if tuple(block_table.shape) != (p.batch, p.max_blocks_per_seq) or tuple(seq_lens.shape) != (p.batch,):
         raise ValueError("block_table / seq_lens shape")
-    if tuple(out.shape) != (p.batch, p.num_q_heads, p.head_dim) or tuple(lse.shape) != (p.batch, p.num_q_heads):
+    if tuple(out.shape) != (_rows(p), p.num_q_heads, p.head_dim) or tuple(lse.shape) != (_rows(p), p.num_q_heads):
         raise ValueError("out/lse shape")
     _abi.check(_abi.dcp_gqa_decode_partial(p, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                            block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),

@@ -23,13 +23,21 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(dcp.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert dcp.dcp_abi_version() == 1
+    assert dcp.dcp_abi_version() == 2
 
 
 def test_struct_layout_matches_header():
-    # 11 int32 fields + 1 float, no padding
-    assert ctypes.sizeof(dcp.dcp_mla_params) == 48
-    assert ctypes.sizeof(dcp.dcp_gqa_params) == 48
+    # 11 int32 fields + 1 float + q_len, no padding; q_len last
+    assert ctypes.sizeof(dcp.dcp_mla_params) == 52
+    assert ctypes.sizeof(dcp.dcp_gqa_params) == 52
+    assert dcp.dcp_mla_params.q_len.offset == 48 and dcp.dcp_gqa_params.q_len.offset == 48
+
+
+def test_workspace_grows_with_query_tokens():
+    one = dcp.dcp_mla_workspace_bytes(mla(batch=8))
+    assert dcp.dcp_mla_workspace_bytes(mla(batch=8, q_len=0)) == one   # 0 means 1
+    assert dcp.dcp_mla_workspace_bytes(mla(batch=8, q_len=4)) == dcp.dcp_mla_workspace_bytes(mla(batch=32))
+    assert dcp.dcp_gqa_workspace_bytes(gqa(batch=4, q_len=2)) == dcp.dcp_gqa_workspace_bytes(gqa(batch=8))
 
 
 def test_status_strings():
@@ -62,6 +70,7 @@ FAKE = 1 << 20  # an aligned non-null address; never dereferenced (validation fa
     (dict(num_heads=0), 1), (dict(max_seq_len_hint=8 * 16 * 64 + 1), 1),
     (dict(num_heads=17), 2), (dict(num_heads=128), 2), (dict(block_size=8), 2), (dict(block_size=2048), 2),
     (dict(kv_lora_rank=256), 2), (dict(rope_dim=32), 2), (dict(batch=4096), 2),
+    (dict(q_len=-1), 1), (dict(q_len=17), 2), (dict(batch=1024, q_len=3), 2),
 ])
 def test_mla_validation(kw, status):
     p = mla(**kw)

@@ -243,6 +243,17 @@ class Case:
             self._q = q
         return self._q
 
+    def queries(self, q_len: int) -> np.ndarray:
+        """Queries of a q_len-token decode step, bf16 bits [batch][q_len][heads][dk]
+        (the head width is dk for MLA and head_dim for GQA); token 0 is ``q``."""
+        w = self.w
+        out = np.empty((w.batch, q_len, w.heads, w.dk), np.uint16)
+        for b in range(w.batch):
+            out[b, 0] = self.q[b]
+            for j in range(1, q_len):
+                out[b, j] = normal_bf16((self.seed, w.wid, T_Q, b, j), (w.heads, w.dk))
+        return out
+
     @property
     def max_seq_len(self) -> int:
         return int(self.seq_lens.max()) if len(self.seq_lens) else 0
