@@ -3,14 +3,18 @@
     python -m kv_cache_context_amd.rocprof_summary stats <kernel_stats.csv>
     python -m kv_cache_context_amd.rocprof_summary traffic <fetch counter_collection.csv> \
         <write counter_collection.csv> <kernel name substring> <calibration copy bytes>
-    python -m kv_cache_context_amd.rocprof_summary report <prof dir> <workload> <mla|gqa>
+    python -m kv_cache_context_amd.rocprof_summary report <prof dir> <name> <mla|gqa> \
+        [<bench arguments> <summary file stem>]
 
 `report` writes the markdown summary of one workload's profiling runs (kernel
 trace statistics, the bench line of the traced run, and the counter traffic
 when the FETCH_SIZE / WRITE_SIZE runs exist) and prints the traffic entry for
 profiles/traffic.json.  The directory layout is the one of the commands quoted
-in the summary: <dir>/<wl>/kt_kernel_stats.csv, <dir>/<wl>_kt.log,
-<dir>/<wl>_FETCH_SIZE/p_counter_collection.csv, <dir>/<wl>_WRITE_SIZE/....
+in the summary: <dir>/<name>/kt_kernel_stats.csv, <dir>/<name>_kt.log,
+<dir>/<name>_FETCH_SIZE/p_counter_collection.csv, <dir>/<name>_WRITE_SIZE/....
+<name> is the workload unless bench arguments other than --workload <name>
+were used; the summary goes to profiles/<kind>_partial_<name>.md unless a
+file stem is given.
 
 `traffic` converts FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into bytes per
 launch of the named kernel, each scaled by the ratio between the known size of
@@ -82,9 +86,11 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int) -> dic
 CAL_COPY_BYTES = 1 << 30
 
 
-def report(prof: str, wl: str, kind: str) -> tuple[str, dict | None]:
+def report(prof: str, wl: str, kind: str, bench_args: str | None = None) -> tuple[str, dict | None]:
+    if bench_args is None:
+        bench_args = f"--workload {wl}" + ("" if wl == "c1" else " --no-cpu-baseline")
     kt_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {prof}/{wl} -o kt -- "
-              f"python -u bench.py --workload {wl}" + ("" if wl == "c1" else " --no-cpu-baseline"))
+              f"python -u bench.py {bench_args}".rstrip())
     pmc_cmd = (f"rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d {prof}/{wl}_<counter> -o p -- "
                f"python -u bench.py --workload {wl} --steps 5 --warmup 1 --no-cpu-baseline --calibration-copy")
     bench = None
@@ -93,7 +99,7 @@ def report(prof: str, wl: str, kind: str) -> tuple[str, dict | None]:
         for line in open(logp):
             if line.startswith("{"):
                 bench = json.loads(line)
-    lines = [f"# {kind} partial + combine, workload {wl}", ""]
+    lines = [f"# {kind} partial + epilogue, {wl}", ""]
     if bench:
         lines += [f"Workload: {bench['config'].get('description', '')}", ""]
     lines += ["Kernel trace (each step: the timed shards' partial calls, i.e. partial_kernel then its split",
@@ -102,8 +108,12 @@ def report(prof: str, wl: str, kind: str) -> tuple[str, dict | None]:
     if bench:
         keep = {k: bench[k] for k in ("value", "unit", "partial_us", "combine_us", "step_hbm_gbps", "mfma_tflops")}
         keep["roofline"] = {k: bench["roofline"][k] for k in ("achieved", "peak", "frac", "bytes_per_launch")}
+        keep["config"] = {k: bench["config"][k] for k in ("workload", "q_len") if k in bench["config"]}
+        keep["epilogue"] = bench.get("epilogue")
         lines += ["bench line of the traced run (HIP-event timing of graph replays; `partial_us` is one",
-                  "partial call = partial_kernel + reduce_kernel):", "", "```", json.dumps(keep), "```", ""]
+                  "partial call = partial_kernel + reduce_kernel).  Kernel tracing adds a few us to every",
+                  "dispatch, so the untraced bench is the timing reference; the kernel averages above are",
+                  "the device durations:", "", "```", json.dumps(keep), "```", ""]
     entry = None
     fetch = os.path.join(prof, f"{wl}_FETCH_SIZE", "p_counter_collection.csv")
     write = os.path.join(prof, f"{wl}_WRITE_SIZE", "p_counter_collection.csv")
@@ -129,8 +139,9 @@ if __name__ == "__main__":
     elif sys.argv[1] == "hash":
         print(source_hash(sys.argv[2]))
     elif sys.argv[1] == "report":
-        text, entry = report(sys.argv[2], sys.argv[3], sys.argv[4])
-        out = os.path.join(os.path.dirname(PKG), "profiles", f"{sys.argv[4]}_partial_{sys.argv[3]}.md")
+        text, entry = report(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5] if len(sys.argv) > 5 else None)
+        stem = sys.argv[6] if len(sys.argv) > 6 else f"{sys.argv[4]}_partial_{sys.argv[3]}"
+        out = os.path.join(os.path.dirname(PKG), "profiles", f"{stem}.md")
         with open(out, "w") as f:
             f.write(text)
         print(json.dumps({f"{sys.argv[4]}:{sys.argv[3]}": entry}))
