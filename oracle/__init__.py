@@ -18,6 +18,9 @@ Every function follows a stated definition:
   latent row serves every query head (same post, section 5.3 "MLA Backend").
 * ``gqa_attention`` — each KV head serves a consecutive group of query heads
   (section 5.4 "GQA Backend").
+* ``decode_e4m3fn`` / ``mla_attention_fp8`` — the fp8 KV cache (the Kimi K3
+  optimizations page serves with an fp8 cache): OCP E4M3 codes decoded exactly,
+  times one per-cache dequantization scale, then ``mla_attention``.
 * ``shard_positions`` — which global token positions a shard holds
   (section 4; round-robin and contiguous layouts).
 * ``query_limit`` / ``query_positions`` — the causal prefix of each query
@@ -40,6 +43,8 @@ from .attention import (  # noqa: F401
     softmax_attention,
     mla_attention,
     gqa_attention,
+    decode_e4m3fn,
+    mla_attention_fp8,
     shard_positions,
     query_limit,
     query_positions,

@@ -83,6 +83,35 @@ def gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
     return o, lse
 
 
+def decode_e4m3fn(bits) -> np.ndarray:
+    """8-bit float codes of the OCP E4M3 format ("e4m3fn") -> exact float64.
+
+    Bit 7 is the sign, bits 6..3 the exponent E (bias 7), bits 2..0 the
+    mantissa M.  E = 0 encodes subnormals M/8 * 2^-6; otherwise the value is
+    (1 + M/8) * 2^(E - 7).  The code with E = 15 and M = 7 (either sign) is
+    NaN; the format has no infinities, so its largest finite magnitude is
+    1.75 * 2^8 = 448.  This is the fp8 KV-cache format read here (the Kimi K3
+    optimizations page runs its cache in fp8; the pages fix no encoding).
+    """
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where((b >> 7) == 1, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (b & 7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def mla_attention_fp8(q: np.ndarray, kv_bits: np.ndarray, kv_scale: float, scale: float,
+                      kv_lora_rank: int = 512):
+    """MLA decode attention over an fp8 latent cache with one dequantization
+    scale for the whole cache: each stored latent row stands for
+    kv_scale * decode_e4m3fn(row), used as both key (all 576) and value (first
+    512) exactly as in ``mla_attention``."""
+    kv = float(kv_scale) * decode_e4m3fn(kv_bits)
+    return mla_attention(q, kv, scale, kv_lora_rank)
+
+
 def shard_positions(L: int, n: int, r: int, layout: int = ROUND_ROBIN) -> np.ndarray:
     """Global token positions held by shard r of n (section 4 "What is DCP?").
 

@@ -16,6 +16,9 @@ the implementation disagrees with:
   token order does not matter, adding a constant to all scores shifts only the
   LSE (also at magnitudes where an unshifted exp overflows);
 * MLA absorbed form equal to explicit per-head up-projection;
+* the fp8 cache format: OCP E4M3 code values from the format's published table
+  (``tests/golden/fp8_e4m3fn.json``), torch's float8_e4m3fn decoding of all 256
+  codes, and the scaling identity of attention over a scaled cache;
 * the fused combine epilogue (merge, value up-projection, sigmoid gate):
   a column-selecting projection with a saturated gate returns columns of the
   plain merge, a zero gate halves the projection, and torch's batched fp64
@@ -33,6 +36,7 @@ import os
 import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "closed_forms.json")
+GOLDEN_FP8 = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fp8_e4m3fn.json")
 TIGHT = 1e-12
 
 
@@ -338,6 +342,52 @@ def pin_bf16_cast(impl):
     # widening is exact
     w = impl.widen_bf16(ref)
     assert np.array_equal(w, torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).double().numpy())
+
+
+def pin_fp8_table(impl):
+    """E4M3 codes decode to the values of the format's published table."""
+    for c in json.load(open(GOLDEN_FP8))["codes"]:
+        got = float(impl.decode_e4m3fn(np.array([int(c["code"], 16)], np.uint8))[0])
+        want = float(c["value"])
+        if math.isnan(want):
+            assert math.isnan(got), c
+        else:
+            assert got == want and math.copysign(1.0, got) == math.copysign(1.0, want), (c, got)
+
+
+def pin_fp8_torch(impl):
+    """All 256 codes decode as torch's float8_e4m3fn does (NaN at the same codes),
+    and the positive finite codes are strictly increasing."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = impl.decode_e4m3fn(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok]) and np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+    assert np.all(np.diff(got[:0x7F]) > 0)
+
+
+def pin_fp8_attention_scale(impl):
+    """Attention over an fp8 cache with dequantization scale s: scores see
+    s * K, values s * V, so o = s * o' and lse = lse' where (o', lse') is
+    attention over the decoded codes with the softmax scale multiplied by s."""
+    r = _rng(45)
+    H, L, R, P = 5, 23, 24, 8
+    q = r.standard_normal((H, R + P))
+    bits = r.integers(0, 256, size=(L, R + P)).astype(np.uint8)
+    bits[(bits & 0x7F) == 0x7F] = 0x3C  # no NaN codes
+    for s in (1.0, 0.0125, 3.5):
+        o, lse = impl.mla_attention_fp8(q, bits, s, 0.3, R)
+        dec = impl.decode_e4m3fn(bits)
+        o2, lse2 = impl.mla_attention(q, dec, 0.3 * s, R)
+        _close(o, s * o2, what=f"fp8 scale {s} o")
+        _close(lse, lse2, what=f"fp8 scale {s} lse")
+    # and against the plain route on explicitly dequantized rows
+    o3, lse3 = impl.softmax_attention(q, 0.0125 * dec, 0.0125 * dec[:, :R], 0.3)
+    o4, lse4 = impl.mla_attention_fp8(q, bits, 0.0125, 0.3, R)
+    _close(o4, o3, what="fp8 plain o")
+    _close(lse4, lse3, what="fp8 plain lse")
 
 
 def _vproj_case(r, N=3, b=4, H=3, Dv=20, Dvo=6):

@@ -45,6 +45,13 @@ MUTANTS = {
     "vproj wrong head": ("y[:, h, :] = o[:, h, :] @ w[h].T", "y[:, h, :] = o[:, h, :] @ w[(h + 1) % w.shape[0]].T"),
     "gate sign": ("sig = 1.0 / (1.0 + np.exp(-g))", "sig = 1.0 / (1.0 + np.exp(g))"),
     "gate missing": ("return sig * y, lse", "return y, lse"),
+    "fp8 exponent bias 8": ("(1.0 + m / 8.0) * np.exp2(e - 7.0)", "(1.0 + m / 8.0) * np.exp2(e - 8.0)"),
+    "fp8 subnormals as normals": ("mag = np.where(e == 0, m / 8.0 * 2.0 ** -6,", "mag = np.where(e == -1, m / 8.0 * 2.0 ** -6,"),
+    "fp8 sign dropped": ("sign = np.where((b >> 7) == 1, -1.0, 1.0)", "sign = 1.0"),
+    "fp8 NaN code as a number": ("mag = np.where((e == 15) & (b & 7 == 7), np.nan, mag)", "pass"),
+    "fp8 scale on scores only": ("    kv = float(kv_scale) * decode_e4m3fn(kv_bits)\n    return mla_attention(q, kv, scale, kv_lora_rank)",
+                                 "    return mla_attention(q, decode_e4m3fn(kv_bits), scale * kv_scale, kv_lora_rank)"),
+    "fp8 scale ignored": ("    kv = float(kv_scale) * decode_e4m3fn(kv_bits)", "    kv = decode_e4m3fn(kv_bits)"),
     "query limit excludes itself": ("return max(0, L - q_len + 1 + j)", "return max(0, L - q_len + j)"),
     "query limit from the front": ("return max(0, L - q_len + 1 + j)", "return max(0, min(L, q_len + j))"),
     "query positions re-sharded by prefix": ("    t = shard_positions(L, n, r, layout)\n    return t[t < query_limit(L, q_len, j)]",

@@ -91,3 +91,45 @@ def test_workload_shapes():
     assert c3.max_blocks_per_seq() == 2048 and c3.local_lens(1)[0] == 32768
     c4b = W.Case(w["c4b"])
     assert c4b.local_lens(1).sum() == 128 * 8192
+
+
+def test_e4m3_encoder_matches_torch():
+    """The fp8 cache encoder is torch's float -> float8_e4m3fn rounding (nearest,
+    ties to even) on in-range values, clamps beyond 448, and maps every finite
+    code's own value back to that code."""
+    import torch
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(100000) * np.exp(rng.uniform(-9, 6, 100000))).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = W.f32_to_e4m3_bits(x)
+    assert np.array_equal(got, ref)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(W.f32_to_e4m3_bits(vals), codes)
+    # midpoints between neighbouring codes go to the even code
+    mids = (vals[1:0x7E] + vals[2:0x7F]) / 2
+    m_codes = W.f32_to_e4m3_bits(mids)
+    assert np.all(m_codes % 2 == 0)
+    assert W.f32_to_e4m3_bits(np.array([1e4, -1e4, 449.0], np.float32)).tolist() == [0x7E, 0xFE, 0x7E]
+
+
+def test_fp8_case_quantizes_the_bf16_draws():
+    """An fp8 case stores the E4M3 codes of the same normal draws divided by the
+    scale; shard pools gather back to the logical codes."""
+    w = W.custom_workload("mla", batch=2, heads=16, seq_lens=(300, 77), block_size=16, num_shards=3, wid=77)
+    c8 = W.Case(w, seed=4, kv_fp8_scale=0.0125)
+    cb = W.Case(w, seed=4)
+    lb = W.bf16_bits_to_f32(cb.kv_logical(0))
+    l8 = c8.kv_logical(0)
+    assert l8.dtype == np.uint8 and l8.shape == (300, 576)
+    import torch
+    dec = torch.from_numpy(l8).view(torch.float8_e4m3fn).float().numpy() * 0.0125
+    # bf16 rounding and fp8 rounding of the same draw: both within their half-ulps
+    assert np.all(np.abs(dec - lb) <= np.abs(lb) * (2.0 ** -4 + 2.0 ** -8) + 2.0 ** -10 * 0.0125)
+    sc = c8.shard(1)
+    assert sc.pools[0].dtype == np.uint8
+    pos = list(W.local_positions(300, 3, 1, 0))
+    for j, t in enumerate(pos):
+        blk = sc.block_table[0, j // 16]
+        assert np.array_equal(sc.pools[0][blk, j % 16], l8[t])

@@ -33,6 +33,9 @@ Input recipe (all values are standard normal draws rounded to bf16):
   relabelled by ``rng.permutation(nb)`` keyed ``[seed, workload_id, PERM, r]``.
   Table entries past a request's last local block hold 0 (a valid block that
   belongs to some other request, so a stray read shows up as a wrong result).
+* fp8 caches (MLA): the same float32 draws divided by the cache's
+  dequantization scale and rounded to the nearest OCP E4M3 code (ties to the
+  even code, magnitudes clamped to 448); the uint8 codes are the ground truth.
 * the ragged-length workload draws lengths from a bimodal mixture shaped like
   the agentic trace the DCP post benchmarks on (section 2.1 "Dataset": median
   near 67k, about half the requests at 64k and above with a long tail, about
@@ -83,6 +86,30 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 def normal_bf16(key, shape) -> np.ndarray:
     rng = np.random.default_rng(list(key))
     return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+# ---------------------------------------------------------------- fp8 (E4M3) codes
+
+def _e4m3_grid() -> np.ndarray:
+    """Magnitudes of the non-negative finite E4M3 codes 0x00..0x7E, in code order."""
+    c = np.arange(0x7F)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2(e - 10.0))
+
+
+_E4M3 = _e4m3_grid()
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round values to the nearest E4M3 code (ties to the even code), clamping
+    magnitudes to 448; returns uint8 codes.  Inputs are finite."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    i = np.clip(np.searchsorted(_E4M3, a), 1, len(_E4M3) - 1)
+    lo, hi = _E4M3[i - 1], _E4M3[i]
+    up = (a - lo > hi - a) | ((a - lo == hi - a) & (i % 2 == 0))
+    code = np.where(up, i, i - 1).astype(np.uint8)
+    return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
 
 
 # ---------------------------------------------------------------- layouts
@@ -202,7 +229,7 @@ class ShardCache:
     rank: int
     local_lens: np.ndarray           # int64 [batch]
     block_table: np.ndarray          # int32 [batch][max_blocks]
-    pools: list = field(default_factory=list)  # MLA: [kv]; GQA: [k, v]; uint16 arrays
+    pools: list = field(default_factory=list)  # MLA: [kv]; GQA: [k, v]; uint16 (bf16) or uint8 (fp8) arrays
 
     @property
     def num_blocks(self) -> int:
@@ -212,13 +239,17 @@ class ShardCache:
 class Case:
     """A seeded instance of a workload."""
 
-    def __init__(self, w: Workload, seed: int = 0, q_scale_pow2: int = 0, needles=()):
+    def __init__(self, w: Workload, seed: int = 0, q_scale_pow2: int = 0, needles=(),
+                 kv_fp8_scale: float | None = None):
         """``q_scale_pow2`` multiplies every query by 2**k (exact in bf16), which
         sharpens the softmax.  ``needles`` is a list of (request, position,
         head): the K/V row at that global position is replaced by that head's
-        query, planting one dominant key (MLA only)."""
+        query, planting one dominant key (MLA only).  ``kv_fp8_scale`` makes
+        the latent cache fp8 (MLA only): rows hold E4M3 codes of value / scale."""
+        assert kv_fp8_scale is None or w.kind == "mla"
         self.w = w
         self.seed = seed
+        self.kv_fp8_scale = None if kv_fp8_scale is None else float(kv_fp8_scale)
         self.q_scale_pow2 = int(q_scale_pow2)
         self.needles = tuple(needles)
         if w.seq_lens is None:
@@ -272,9 +303,20 @@ class Case:
         w = self.w
         return (w.dk,) if w.kind == "mla" else (w.kv_heads, w.head_dim)
 
+    @property
+    def kv_dtype(self):
+        return np.uint16 if self.kv_fp8_scale is None else np.uint8
+
     def _chunk(self, tid: int, b: int, c: int, L: int) -> np.ndarray:
         t0 = c * CHUNK
         n = min(CHUNK, L - t0)
+        if self.kv_fp8_scale is not None:
+            rng = np.random.default_rng([self.seed, self.w.wid, tid, b, c])
+            x = rng.standard_normal((n,) + self._row_shape(), dtype=np.float32)
+            for nb, pos, head in self.needles:
+                if nb == b and t0 <= pos < t0 + n:
+                    x[pos - t0] = bf16_bits_to_f32(self.q[b, head])
+            return f32_to_e4m3_bits(x / np.float32(self.kv_fp8_scale))
         a = normal_bf16((self.seed, self.w.wid, tid, b, c), (n,) + self._row_shape())
         for nb, pos, head in self.needles:
             if nb == b and t0 <= pos < t0 + n:
@@ -282,7 +324,8 @@ class Case:
         return a
 
     def kv_logical(self, b: int, t0: int = 0, t1: int | None = None):
-        """bf16 bits of request b's tokens [t0, t1) in global order.
+        """Stored bits of request b's tokens [t0, t1) in global order (bf16
+        bits, or E4M3 codes for an fp8 cache).
 
         MLA: one array [n][576]; GQA: (K, V) each [n][kv_heads][head_dim].
         """
@@ -296,16 +339,16 @@ class Case:
                 lo = max(t0, c * CHUNK) - c * CHUNK
                 hi = min(t1, (c + 1) * CHUNK) - c * CHUNK
                 parts.append(a[lo:hi])
-            outs.append(np.concatenate(parts) if parts else np.zeros((0,) + self._row_shape(), np.uint16))
+            outs.append(np.concatenate(parts) if parts else np.zeros((0,) + self._row_shape(), self.kv_dtype))
         return outs[0] if self.w.kind == "mla" else tuple(outs)
 
     def rows_at(self, b: int, positions) -> list:
-        """bf16 bits of request b at the given global token positions (any order)."""
+        """Stored bits of request b at the given global token positions (any order)."""
         pos = np.asarray(positions, dtype=np.int64)
         L = int(self.seq_lens[b])
         res = []
         for tid in self._tensor_ids():
-            out = np.empty((len(pos),) + self._row_shape(), np.uint16)
+            out = np.empty((len(pos),) + self._row_shape(), self.kv_dtype)
             for c in np.unique(pos // CHUNK):
                 sel = np.nonzero(pos // CHUNK == c)[0]
                 out[sel] = self._chunk(tid, b, int(c), L)[pos[sel] - c * CHUNK]
@@ -334,7 +377,7 @@ class Case:
         return table, max(total, 1)
 
     def shard(self, r: int, max_blocks: int | None = None, threads: int | None = None) -> ShardCache:
-        """Build shard r's pool(s) and table (host memory, bf16 bits)."""
+        """Build shard r's pool(s) and table (host memory, stored bits)."""
         return self.shards([r], max_blocks, threads)[0]
 
     def shards(self, ranks, max_blocks: int | None = None, threads: int | None = None) -> list:
@@ -345,7 +388,7 @@ class Case:
         out = []
         for r in ranks:
             table, nb = self.block_table(r, max_blocks)
-            pools = [np.zeros((nb, B) + self._row_shape(), np.uint16) for _ in self._tensor_ids()]
+            pools = [np.zeros((nb, B) + self._row_shape(), self.kv_dtype) for _ in self._tensor_ids()]
             out.append(ShardCache(rank=r, local_lens=self.local_lens(r), block_table=table, pools=pools))
         jobs = [(b, c) for b in range(w.batch) for c in range(-(-int(self.seq_lens[b]) // CHUNK))]
 

@@ -14,6 +14,11 @@ def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
     return t.to(device).view(torch.bfloat16)
 
 
+def fp8_tensor(codes: np.ndarray, device) -> torch.Tensor:
+    """uint8 E4M3 codes -> torch.float8_e4m3fn tensor on `device` (bit-exact)."""
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).to(device).view(torch.float8_e4m3fn)
+
+
 def int32_tensor(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
 
