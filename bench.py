@@ -63,7 +63,7 @@ def algorithmic_bytes(case, r, q_len=1):
     ll = case.local_lens(r)
     nblk = -(-ll // w.block_size)
     if w.kind == "mla":
-        kv = int(ll.sum()) * w.dk * 2
+        kv = int(ll.sum()) * w.dk * (1 if case.kv_fp8_scale is not None else 2)
     else:
         kv = int(ll.sum()) * w.kv_heads * w.head_dim * 2 * 2
     q = w.batch * q_len * w.heads * w.dk * 2
@@ -133,7 +133,9 @@ def cpu_baseline(case, budget_s=10.0, q_len=1):
                 pos = oracle.shard_positions(L, w.num_shards, r, w.layout)
                 if r in ranks:
                     rows = case.rows_at(b, pos)
-                    shard_in.append((r, pos, [oracle.widen_bf16(x) for x in rows]))
+                    if case.kv_fp8_scale is None:
+                        rows = [oracle.widen_bf16(x) for x in rows]
+                    shard_in.append((r, pos, rows))
                 else:
                     shard_in.append((r, pos, None))
             cache[b] = ([oracle.widen_bf16(qs[b, j]) for j in range(q_len)], shard_in)
@@ -147,6 +149,9 @@ def cpu_baseline(case, budget_s=10.0, q_len=1):
                 m = int(np.searchsorted(pos, lim))  # shard positions below token j's limit
                 if rows is None:
                     parts.append((np.zeros((w.heads, w.dv)), np.full(w.heads, -np.inf)))
+                elif w.kind == "mla" and case.kv_fp8_scale is not None:
+                    parts.append(oracle.mla_attention_fp8(qj[j], rows[0][:m], case.kv_fp8_scale, w.scale,
+                                                          w.kv_lora_rank))
                 elif w.kind == "mla":
                     parts.append(oracle.mla_attention(qj[j], rows[0][:m], w.scale, w.kv_lora_rank))
                 else:
@@ -181,6 +186,9 @@ def main():
     ap.add_argument("--epilogue", choices=("combine", "vproj"), default="combine",
                     help="step epilogue: LSE combine + bf16 cast, or the combine fused with the per-head value "
                          "up-projection (128 wide) and sigmoid gate (MLA workloads)")
+    ap.add_argument("--kv-dtype", choices=("bf16", "fp8"), default="bf16",
+                    help="latent cache format of the MLA workloads: bf16, or fp8 E4M3 with one dequantization "
+                         "scale")
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per request (multi-token decode step, causal within the step)")
     ap.add_argument("--warm-cache", action="store_true", help="no KV rotation (reported as such)")
@@ -195,7 +203,7 @@ def main():
 
     import torch
     import workloads as W
-    from workloads.device import bf16_tensor, int32_tensor
+    from workloads.device import bf16_tensor, fp8_tensor, int32_tensor
     from kv_cache_context_amd import ops
 
     w = W.WORKLOADS[args.workload]
@@ -206,7 +214,11 @@ def main():
     rows = w.batch * ql
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    case = W.Case(w, seed=args.seed)
+    fp8 = args.kv_dtype == "fp8"
+    if fp8 and w.kind != "mla":
+        print(json.dumps({"error": "--kv-dtype fp8 applies to the MLA workloads"}))
+        sys.exit(2)
+    case = W.Case(w, seed=args.seed, kv_fp8_scale=W.FP8_SCALE if fp8 else None)
     n = w.num_shards
     mb = case.max_blocks_per_seq()
     hint = max(1, case.max_seq_len)
@@ -227,7 +239,7 @@ def main():
         ent = {"table": int32_tensor(sc.block_table, dev)}
         if w.kind == "mla":
             ent["p"] = ops.mla_params(batch=w.batch, num_heads=w.heads, **common)
-            ent["pools"] = [bf16_tensor(sc.pools[0], dev)]
+            ent["pools"] = [fp8_tensor(sc.pools[0], dev) if fp8 else bf16_tensor(sc.pools[0], dev)]
             ent["ws"] = ops.mla_workspace(ent["p"], dev)
         else:
             ent["p"] = ops.gqa_params(batch=w.batch, num_q_heads=w.heads, num_kv_heads=w.kv_heads, **common)
@@ -240,7 +252,10 @@ def main():
         e = shards[r]
         pool = e["pools"][copy]
         st = torch.cuda.current_stream()
-        if w.kind == "mla":
+        if fp8:
+            ops.dcp_mla_decode_partial_fp8(e["p"], q_d, pool, case.kv_fp8_scale, e["table"], lens_d, po[r], pl[r],
+                                           e["ws"], st)
+        elif w.kind == "mla":
             ops.dcp_mla_decode_partial(e["p"], q_d, pool, e["table"], lens_d, po[r], pl[r], e["ws"], st)
         else:
             ops.dcp_gqa_decode_partial(e["p"], q_d, pool[0], pool[1], e["table"], lens_d, po[r], pl[r], e["ws"],
@@ -355,7 +370,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "kind": w.kind, "batch": w.batch,
-                   "heads": w.heads, "q_len": ql, "num_shards": n, "timed_shards": timed, "block_size": w.block_size,
+                   "heads": w.heads, "q_len": ql, "kv_dtype": args.kv_dtype, "num_shards": n, "timed_shards": timed, "block_size": w.block_size,
                    "local_tokens": int(sum(case.local_lens(r).sum() for r in timed)),
                    "kv_copies_rotated": copies},
         "step_hbm_gbps": round(step_gbs, 1),
@@ -367,7 +382,7 @@ def main():
         "timing": "K steps captured in one HIP graph, replayed; HIP events around the replay",
         "mfma_tflops": round(flops / (part_mean * 1e-6) / 1e12, 2),
         "mfma_frac": round(flops / (part_mean * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-        "roofline": {"bound": "hbm", "kernel": f"dcp_{w.kind}_decode_partial",
+        "roofline": {"bound": "hbm", "kernel": f"dcp_{w.kind}_decode_partial" + ("_fp8" if fp8 else ""),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": alg_partial},
@@ -378,7 +393,7 @@ def main():
         b2.copy_(a)
         torch.cuda.synchronize()
         del a, b2
-    kind = "mla" if w.kind == "mla" else "gqa"
+    kind = ("mla8" if fp8 else "mla") if w.kind == "mla" else "gqa"
     res["roofline"]["traffic"] = stored_traffic(kind, w.name) if ql == 1 else None
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on the host")

@@ -13,6 +13,9 @@
  *
  *   dcp_mla_decode_partial  one rank's partial for MLA (one latent row per
  *                           token shared by all query heads; section 5.3)
+ *   dcp_mla_decode_partial_fp8
+ *                           the same over an fp8 (OCP E4M3) latent cache with
+ *                           one dequantization scale
  *   dcp_gqa_decode_partial  one rank's partial for GQA (KV heads shared by
  *                           consecutive groups of query heads; section 5.4)
  *   dcp_combine             the LSE-weighted merge of N partials, fused with
@@ -136,6 +139,29 @@ dcp_status dcp_mla_decode_partial(const dcp_mla_params* p, const void* q, const 
                                   const int32_t* block_table, const int32_t* seq_lens, float* out,
                                   float* lse, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
+
+/* dcp_mla_decode_partial over an fp8 latent cache.  The Kimi K3 optimizations
+ * page ("Kimi K3 Performance Optimizations in vLLM", decode context
+ * parallelism and its serving recipe) runs the KV cache in fp8; the pages fix
+ * no encoding, so this library reads the OCP 8-bit float E4M3 format (1 sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, no infinities, S.1111.111 =
+ * NaN, largest magnitude 448) with one scale for the whole cache: stored code
+ * x stands for kv_scale * x.  The result is dcp_mla_decode_partial's over the
+ * dequantized rows:
+ *     z_t   = softmax_scale * <q[b][h], kv_scale * kv[t]>
+ *     out   = sum_t exp(z_t - lse) * kv_scale * kv[t][0:R]
+ *
+ *  kv_cache    E4M3 codes, uint8 [num_blocks][block_size][R+P] (576 bytes per
+ *              row), 16-byte aligned
+ *  kv_scale    > 0 and finite; softmax_scale * kv_scale must lie in
+ *              [1e-30, 1e30]; otherwise DCP_ERR_INVALID_ARGUMENT
+ * Every other argument, the workspace size (dcp_mla_workspace_bytes) and the
+ * error behaviour are those of dcp_mla_decode_partial.  NaN codes in the
+ * cache give unspecified results (never a fault). */
+dcp_status dcp_mla_decode_partial_fp8(const dcp_mla_params* p, const void* q, const void* kv_cache,
+                                      float kv_scale, const int32_t* block_table, const int32_t* seq_lens,
+                                      float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /* ------------------------------------------------------------------ GQA */
 

@@ -132,6 +132,47 @@ dcp_status gqa_check(const dcp_gqa_params* p) {
   return DCP_OK;
 }
 
+// Both MLA entry points: bf16 cache, or E4M3 cache with dequantization scale kv_scale.
+dcp_status mla_partial(const dcp_mla_params* p, const void* q, const void* kv_cache, bool fp8, float kv_scale,
+                       const int32_t* block_table, const int32_t* seq_lens, float* out, float* lse,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  dcp_status st = mla_check(p);
+  if (st != DCP_OK) return st;
+  if (fp8) {
+    // the scaled softmax scale must stay a finite, normal fp32 number
+    const double c = (double)p->softmax_scale * (double)kv_scale;
+    if (!(kv_scale > 0.f) || !std::isfinite(kv_scale) || !(c >= 1e-30 && c <= 1e30))
+      return DCP_ERR_INVALID_ARGUMENT;
+  }
+  if (p->batch == 0) return DCP_OK;
+  if (!q || !kv_cache || !block_table || !seq_lens || !out || !lse) return DCP_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4) || !aligned(lse, 4))
+    return DCP_ERR_INVALID_ARGUMENT;
+  const int rows = rows_of(p->batch, p->q_len);
+  const dcp::WsLayout wl = dcp::ws_layout(rows, p->num_heads, 512);
+  if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
+  hipError_t herr = hipSuccess;
+  const int cus = device_cus(&herr);
+  if (cus <= 0) return hip_status(herr);
+
+  dcp::MlaArgs a;
+  a.s = split_args(rows, p->block_size, p->max_blocks_per_seq, p->num_blocks, p->shard_rank,
+                   p->num_shards, p->layout, fp8 ? p->softmax_scale * kv_scale : p->softmax_scale, block_table,
+                   seq_lens, out, lse, workspace, wl);
+  a.s.q_len = qlen_of(p->q_len);
+  a.s.G = env_int("DCP_SPLIT_WGS", cus < dcp::kMaxSplitWGs ? cus : dcp::kMaxSplitWGs, 1,
+                  dcp::kMaxSplitWGs);
+  a.s.min_tiles = env_int(fp8 ? "DCP_MLA8_MIN_TILES" : "DCP_MLA_MIN_TILES", fp8 ? 8 : 4, 1, 1 << 20);
+  a.s.seg_cost = env_int(fp8 ? "DCP_MLA8_SEG_COST" : "DCP_MLA_SEG_COST", fp8 ? 4 : 2, 0, 64);
+  a.q = (const uint16_t*)q;
+  a.kv = kv_cache;
+  a.heads = p->num_heads;
+  a.fp8 = fp8;
+  a.vscale = fp8 ? kv_scale : 1.0f;
+  return hip_status(dcp::launch_mla_partial(a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,33 +201,16 @@ dcp_status dcp_mla_decode_partial(const dcp_mla_params* p, const void* q, const 
                                   const int32_t* block_table, const int32_t* seq_lens, float* out,
                                   float* lse, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream) {
-  dcp_status st = mla_check(p);
-  if (st != DCP_OK) return st;
-  if (p->batch == 0) return DCP_OK;
-  if (!q || !kv_cache || !block_table || !seq_lens || !out || !lse) return DCP_ERR_INVALID_ARGUMENT;
-  if (!aligned(q, 16) || !aligned(kv_cache, 16) || !aligned(out, 16) || !aligned(block_table, 4) ||
-      !aligned(seq_lens, 4) || !aligned(lse, 4))
-    return DCP_ERR_INVALID_ARGUMENT;
-  const int rows = rows_of(p->batch, p->q_len);
-  const dcp::WsLayout wl = dcp::ws_layout(rows, p->num_heads, 512);
-  if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
-  hipError_t herr = hipSuccess;
-  const int cus = device_cus(&herr);
-  if (cus <= 0) return hip_status(herr);
+  return mla_partial(p, q, kv_cache, false, 1.0f, block_table, seq_lens, out, lse, workspace, workspace_bytes,
+                     stream);
+}
 
-  dcp::MlaArgs a;
-  a.s = split_args(rows, p->block_size, p->max_blocks_per_seq, p->num_blocks, p->shard_rank,
-                   p->num_shards, p->layout, p->softmax_scale, block_table, seq_lens, out, lse,
-                   workspace, wl);
-  a.s.q_len = qlen_of(p->q_len);
-  a.s.G = env_int("DCP_SPLIT_WGS", cus < dcp::kMaxSplitWGs ? cus : dcp::kMaxSplitWGs, 1,
-                  dcp::kMaxSplitWGs);
-  a.s.min_tiles = env_int("DCP_MLA_MIN_TILES", 4, 1, 1 << 20);
-  a.s.seg_cost = env_int("DCP_MLA_SEG_COST", 2, 0, 64);
-  a.q = (const uint16_t*)q;
-  a.kv = (const uint16_t*)kv_cache;
-  a.heads = p->num_heads;
-  return hip_status(dcp::launch_mla_partial(a, stream));
+dcp_status dcp_mla_decode_partial_fp8(const dcp_mla_params* p, const void* q, const void* kv_cache,
+                                      float kv_scale, const int32_t* block_table, const int32_t* seq_lens,
+                                      float* out, float* lse, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  return mla_partial(p, q, kv_cache, true, kv_scale, block_table, seq_lens, out, lse, workspace, workspace_bytes,
+                     stream);
 }
 
 size_t dcp_gqa_workspace_bytes(const dcp_gqa_params* p) {

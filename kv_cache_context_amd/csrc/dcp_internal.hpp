@@ -52,8 +52,10 @@ struct SplitArgs {
 struct MlaArgs {
   SplitArgs s;
   const uint16_t* q;
-  const uint16_t* kv;
+  const void* kv;  // bf16 or E4M3 rows of 576
   int heads;
+  bool fp8;        // E4M3 cache (s.c then includes the dequantization scale)
+  float vscale;    // multiplier of the output: the dequantization scale (fp8), else 1
 };
 
 struct GqaArgs {

@@ -29,6 +29,21 @@
 //  * LDS rows are 1152 B; 16-byte chunks are XOR-swizzled per row so both the
 //    row-wise K reads and the transposing V reads hit distinct banks.
 //  * Split-K partials go to the workspace and a small kernel merges them.
+//
+// fp8 latent cache (the Kimi K3 optimizations page serves with an fp8 KV
+// cache): rows hold 576 OCP E4M3 codes and one scale s dequantizes the whole
+// cache.  The same kernel runs on 576-byte rows (18 KiB tiles, 7 in LDS):
+//  * K operands are read as 16-byte chunks (64 latent values per two MFMA
+//    k-steps; q is loaded in the matching k order) and V^T operands with the
+//    byte-transposing ds_read_b64_tr_b8; both are widened to bf16 in registers
+//    by v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3 value is a bf16 value),
+//    one step ahead of the MFMA that consumes them, so the conversions of one
+//    step issue while the previous step's MFMA runs.  The contractions stay
+//    bf16 x bf16 with fp32 accumulation: the fp8 matrix instructions of gfx950
+//    align the products of one instruction to the largest of them with about
+//    11 bits below it, too coarse for the scores of peaked softmaxes;
+//  * s multiplies the softmax scale (scores see s*K) and the output once
+//    (values are s*V), so no per-element scaling is done.
 #include "dcp_device.hpp"
 #include "dcp_internal.hpp"
 #include "dcp_split.hpp"
@@ -37,31 +52,48 @@ namespace dcp {
 namespace mla {
 
 constexpr int R = 512, P = 64, DK = R + P;
-constexpr int ROW = DK * 2;           // bytes per latent row
 constexpr int TILE = 32;              // tokens per pipeline tile
-constexpr int STAGE = TILE * ROW;     // 36864 bytes
+constexpr int THREADS = 512;
+constexpr int NWAVE = THREADS / 64;
+constexpr int KS = DK / 32;           // k-steps of the score contraction (18)
+constexpr int VB = R / 16;            // 16-column blocks of the value contraction (32)
 #ifndef DCP_MLA_NST
 #define DCP_MLA_NST 4
 #endif
-constexpr int NST = DCP_MLA_NST;      // tiles resident in LDS (NST - 1 in flight)
-static_assert(NST >= 2 && NST <= 4, "ring depth");
-constexpr int CPR = ROW / 16;         // 16-byte chunks per row (72)
-constexpr int THREADS = 512;
-constexpr int NWAVE = THREADS / 64;
-constexpr int CPT = TILE * CPR / 64;  // 1 KiB copy instructions per tile (36)
-constexpr int DMA_N = (CPT + NWAVE - 1) / NWAVE;  // copy slots per wave (5; the last is partial)
-constexpr int KS = DK / 32;           // k-steps of the score contraction (18)
-constexpr int VB = R / 16;            // 16-column blocks of the value contraction (32)
-static_assert(TILE * CPR % 64 == 0, "tile copy split");
+
+// Cache row format: bf16 (FP8 = false) or E4M3 codes (FP8 = true).
+template <bool FP8>
+struct Fmt {
+  static constexpr int ROW = DK * (FP8 ? 1 : 2);      // bytes per latent row (1152 or 576)
+  static constexpr int STAGE = TILE * ROW;            // bytes per tile (36 KiB or 18 KiB)
+  static constexpr int NST = FP8 ? 7 : DCP_MLA_NST;   // tiles resident in LDS (NST - 1 in flight)
+  static constexpr int CPR = ROW / 16;                // 16-byte chunks per row (72 or 36)
+  static constexpr int CPT = TILE * CPR / 64;         // 1 KiB copy instructions per tile (36 or 18)
+  static constexpr int DMA_N = (CPT + NWAVE - 1) / NWAVE;  // copy slots per wave (5 or 3; the last partial)
+  static_assert(NST >= 2 && NST <= 8, "ring depth");
+  static_assert(TILE * CPR % 64 == 0, "tile copy split");
+  static_assert(2 * DMA_N <= KS, "copy slots fit the score steps");
+};
 
 // Chunk swizzle of LDS row r: 16-byte chunk c of row r is stored at chunk
-// (c & ~7) | ((c & 7) ^ swz(r)), so a row's 72 chunks stay inside their aligned
-// groups of 8.  swz(r) = r mod 8 was selected on gfx950 by counting LDS bank
-// conflicts (SQ_LDS_BANK_CONFLICT) for the two read patterns of this kernel
-// across a set of candidate swizzles: it is conflict-free for both the row-wise
-// score reads (ds_read_b128, 16 rows x 4 chunks per instruction) and the
-// transposing value reads (ds_read_b64_tr_b16, 16 rows x 2 chunks).
-__host__ __device__ constexpr int swz(int r) { return r & 7; }
+// c ^ swz(r), which stays inside c's aligned group of 8 (bf16) or 4 (fp8)
+// chunks.
+// bf16 rows (72 chunks): swz(r) = r mod 8 was selected on gfx950 by counting
+// LDS bank conflicts (SQ_LDS_BANK_CONFLICT) for the two read patterns of this
+// kernel across a set of candidate swizzles: it is conflict-free for both the
+// row-wise score reads (ds_read_b128, 16 rows x 4 chunks per instruction) and
+// the transposing value reads (ds_read_b64_tr_b16, 16 rows x 2 chunks).
+// fp8 rows (36 chunks, 576 B): swz(r) = bit 3 of r | (bit 3 xor bit 4 of r) << 1.
+// Chosen with a model of the gfx950 LDS fitted to the conflict counts measured
+// for the bf16 layout (128 banks of 4 bytes; a 16-byte read serves its lanes in
+// four groups of 16 and an 8-byte read in two groups of 32): under it both fp8
+// read patterns, the score reads (rows 16t + 0..15, chunk 4j + lane group) and
+// the transposing value reads (rows 4g + 0..3 and 16 + 4g + 0..3 of lane group
+// g), touch every bank at most once per group.
+template <bool FP8>
+__host__ __device__ constexpr int swz(int r) {
+  return FP8 ? (((r >> 3) & 1) | ((((r >> 3) ^ (r >> 4)) & 1) << 1)) : (r & 7);
+}
 
 constexpr int TBL = 256;  // block-table entries staged in LDS per window
 
@@ -72,15 +104,28 @@ struct Xchg {
   float l[4][2][16];   // segment sums per head
 };
 
+template <bool FP8>
 struct Smem {
-  char tiles[NST * STAGE];
+  char tiles[Fmt<FP8>::NST * Fmt<FP8>::STAGE];
   int pref[kMaxBatch + 1];
   int tbl[TBL];
   int wsum[NWAVE];
   int flag;
   Xchg xc;
 };
-static_assert(sizeof(Smem) <= 160 * 1024, "LDS budget");
+static_assert(sizeof(Smem<false>) <= 160 * 1024 && sizeof(Smem<true>) <= 160 * 1024, "LDS budget");
+
+// Waits until at most min(K, rem) tiles' copies (D copy instructions each) are
+// outstanding: vector memory operations of a wave complete in issue order.
+template <int K, int D>
+__device__ __forceinline__ void wait_tiles(int rem) {
+  if constexpr (K <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (rem >= K) wait_vmcnt<K * D>();
+    else wait_tiles<K - 1, D>(rem);
+  }
+}
 
 // Where the copies of one tile go: source block(s) and LDS stage.  All fields
 // are wave-uniform.
@@ -100,7 +145,8 @@ struct TableWin {
   int end;  // one past the last block held
 };
 
-__device__ __forceinline__ void load_window(const MlaArgs& a, const int32_t* trow, Smem& sm, int lo, int hi) {
+template <bool FP8>
+__device__ __forceinline__ void load_window(const MlaArgs& a, const int32_t* trow, Smem<FP8>& sm, int lo, int hi) {
   const SplitArgs& s = a.s;
   const int n = min(hi - lo, TBL);
   for (int i = (int)threadIdx.x; i < n; i += THREADS) {
@@ -121,7 +167,8 @@ struct Planner {
   int pf0, pf1;    // entries of blocks pf_pg and pf_pg + 1 (wave-uniform values)
 };
 
-__device__ __forceinline__ void plan_prefetch(Planner& pl, const Smem& sm) {
+template <bool FP8>
+__device__ __forceinline__ void plan_prefetch(Planner& pl, const Smem<FP8>& sm) {
   // indices clamped into the array; a value read for a block outside the
   // window is never used (the next plan slides the window and drops it)
   pl.pf0 = sm.tbl[min(max(pl.pg - pl.win.lo, 0), TBL - 1)];
@@ -129,8 +176,10 @@ __device__ __forceinline__ void plan_prefetch(Planner& pl, const Smem& sm) {
   pl.pf_pg = pl.pg;
 }
 
-__device__ __forceinline__ TileCopy plan_next(const MlaArgs& a, const int32_t* trow, Smem& sm, Planner& pl,
+template <bool FP8>
+__device__ __forceinline__ TileCopy plan_next(const MlaArgs& a, const int32_t* trow, Smem<FP8>& sm, Planner& pl,
                                               DCP_LDS char* stage, bool valid) {
+  constexpr int ROW = Fmt<FP8>::ROW;
   TileCopy t;
   t.valid = valid;
   t.stage = stage;
@@ -180,12 +229,13 @@ __device__ __forceinline__ TileCopy plan_next(const MlaArgs& a, const int32_t* t
 
 // Issue copy i (0 <= i < DMA_N) of a planned tile: 1 KiB per wave (chunks
 // 64 * (i * NWAVE + wave) .. +63 of the tile).
-__device__ __forceinline__ void copy_part(const TileCopy& t, int i, const int (&goff)[DMA_N],
-                                          const int (&grow)[DMA_N]) {
+template <bool FP8>
+__device__ __forceinline__ void copy_part(const TileCopy& t, int i, const int (&goff)[Fmt<FP8>::DMA_N],
+                                          const int (&grow)[Fmt<FP8>::DMA_N]) {
   if (!t.valid) return;
   const int wave = uni(threadIdx.x >> 6);
   const int slot = i * NWAVE + wave;
-  if (slot >= CPT) return;  // the last round covers only part of the waves
+  if (slot >= Fmt<FP8>::CPT) return;  // the last round covers only part of the waves
   DCP_LDS char* dst = t.stage + slot * 1024;
   if (t.split >= TILE) {
     dma16_sbase(t.base0, (uint32_t)goff[i], dst);
@@ -194,17 +244,80 @@ __device__ __forceinline__ void copy_part(const TileCopy& t, int i, const int (&
   }
 }
 
-__device__ __forceinline__ void copy_all(const TileCopy& t, const int (&goff)[DMA_N], const int (&grow)[DMA_N]) {
+template <bool FP8>
+__device__ __forceinline__ void copy_all(const TileCopy& t, const int (&goff)[Fmt<FP8>::DMA_N],
+                                         const int (&grow)[Fmt<FP8>::DMA_N]) {
 #pragma unroll
-  for (int i = 0; i < DMA_N; ++i) copy_part(t, i, goff, grow);
+  for (int i = 0; i < Fmt<FP8>::DMA_N; ++i) copy_part<FP8>(t, i, goff, grow);
 }
 
 // Zero the tile rows at and past `valid` (the unused end of the last block),
 // so stale cache contents can never reach the value contraction.
+template <bool FP8>
 __device__ __forceinline__ void zero_tail(DCP_LDS char* stage, int valid) {
+  constexpr int CPR = Fmt<FP8>::CPR;
   const int start = valid * CPR;
   for (int c = start + (int)threadIdx.x; c < TILE * CPR; c += THREADS)
     *(DCP_LDS f32x4*)(stage + c * 16) = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Tile modes: FULL computes the scores, softmax and values of a tile;
+// MAXIMUM only the scores' running maximum (see compute_tile).
+enum { FULL = 0, MAXIMUM = 1 };
+
+// Eight E4M3 codes (two dwords, code k in byte k % 4 of dword k / 4) widened
+// to bf16, in order.  The conversion is exact.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Byte-transposing LDS read: inside each group of 16 lanes, lane i receives
+// byte (i % 8) of the 8 bytes loaded by lanes 2k + i / 8, k = 0..7.  With lanes
+// 2k and 2k + 1 of a group pointing at bytes 0..7 and 8..15 of row k's 16-byte
+// column block, lane i gets column i of the 8 rows.
+__device__ __forceinline__ uint2 lds_read_tr8(const DCP_LDS char* p) {
+  typedef __attribute__((ext_vector_type(2))) int i32x2;
+  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((DCP_LDS i32x2*)p);
+  return make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+}
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// This lane's query operands for the 18 k-steps of the score contraction of one
+// head.  bf16 cache: step ks holds latent k = 32 ks + 8 g4 + 0..7.  fp8 cache:
+// steps 2j and 2j + 1 hold k = 64 j + 16 g4 + 0..7 and + 8..15 (the k order in
+// which one 16-byte chunk of an fp8 row feeds two steps).  The sum over k does
+// not depend on the order.
+struct QOps {
+  bf16x8 f[KS];
+};
+
+template <bool FP8>
+__device__ __forceinline__ void load_q(const uint16_t* qrow, int g4, QOps& q) {
+  if constexpr (FP8) {
+    const uint16_t* qp = qrow + 16 * g4;
+#pragma unroll
+    for (int j = 0; j < KS / 2; ++j) {
+      q.f[2 * j] = *(const bf16x8*)(qp + 64 * j);
+      q.f[2 * j + 1] = *(const bf16x8*)(qp + 64 * j + 8);
+    }
+  } else {
+    const bf16x8* qp = (const bf16x8*)(qrow + 8 * g4);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) q.f[ks] = qp[4 * ks];
+  }
+}
+__device__ __forceinline__ void zero_q(QOps& q) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) q.f[ks] = bf16x8{};
+}
+__device__ __forceinline__ void tie_q(QOps& q) {
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(q.f[ks]));
 }
 
 // One 32-token tile: this wave's scores over its 16 tokens for its 16 heads,
@@ -218,57 +331,97 @@ __device__ __forceinline__ void zero_tail(DCP_LDS char* stage, int valid) {
 // MAXIMUM: scores only; m becomes the running maximum of this wave's half.
 // Every wave of the workgroup calls this with the same `first` and `preset`
 // (it holds workgroup barriers).
-enum { FULL = 0, MAXIMUM = 1 };
-template <int MODE>
+template <bool FP8, int MODE>
 __device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int tok0, int lr, bool first, bool preset,
-                                             const bf16x8 (&qf)[KS], f32x4 (&acc)[VB / 2], float& m, float& l,
+                                             const QOps& qo, f32x4 (&acc)[VB / 2], float& m, float& l,
                                              float c, float thr, bool& ovf, Xchg& xc, int th, int hq,
-                                             const TileCopy& nxt, const int (&goff)[DMA_N],
-                                             const int (&grow)[DMA_N]) {
+                                             const TileCopy& nxt, const int (&goff)[Fmt<FP8>::DMA_N],
+                                             const int (&grow)[Fmt<FP8>::DMA_N]) {
+  constexpr int ROW = Fmt<FP8>::ROW;
+  constexpr int DMA_N = Fmt<FP8>::DMA_N;
   const int lane = threadIdx.x & 63;
   const int g4 = lane >> 4, r16 = lane & 15;
 
   // ---- scores S^T[tok][head] for tokens 16*th + (0..15): two MFMA chains
   // (k-step parity); K operands stream through a window of KD k-steps.  The
   // next tile's copies are spread over the steps.
-  const int fz = swz(r16);  // row 16*th + r16 has the swizzle of r16
-  const int offE = ((g4) ^ fz) * 16;
-  const int offO = ((4 | g4) ^ fz) * 16;
+  const int fz = swz<FP8>(16 * th + r16);
   const DCP_LDS char* kp = st + (16 * th + r16) * ROW;
   constexpr int KD = 8;
-  static_assert(2 * DMA_N <= KS, "copy slots");
-  bf16x8 kr[KD];
-  auto kload = [&](int ks) {
-    kr[ks % KD] = *(const DCP_LDS bf16x8*)(kp + (ks >> 1) * 128 + ((ks & 1) ? offO : offE));
-  };
-#pragma unroll
-  for (int ks = 0; ks < KD; ++ks) kload(ks);
   f32x4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  if constexpr (FP8) {
+    // one 16-byte read feeds k-steps 2j and 2j + 1: chunk 4j + g4 of the row
+    // (physical chunk 4j + (g4 ^ swz)); each step's operand is converted while
+    // the previous step's MFMA runs
+    const DCP_LDS char* kc = kp + ((g4 ^ fz) * 16);
+    u32x4 kr[KD / 2];
+    auto kload = [&](int j) { kr[j % (KD / 2)] = *(const DCP_LDS u32x4*)(kc + 64 * j); };
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    __builtin_amdgcn_sched_barrier(0);
-    if ((ks & 1) == 0 && ks / 2 < DMA_N) copy_part(nxt, ks / 2, goff, grow);
-    sc[ks & 1] = mfma_16x16x32(kr[ks % KD], qf[ks], sc[ks & 1]);
-    if (ks + KD < KS) kload(ks + KD);
+    for (int j = 0; j < KD / 2; ++j) kload(j);
+    bf16x8 kb = e4m3x8_to_bf16(kr[0][0], kr[0][1]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      if ((ks & 1) == 0 && ks / 2 < DMA_N) copy_part<FP8>(nxt, ks / 2, goff, grow);
+      sc[ks & 1] = mfma_16x16x32(kb, qo.f[ks], sc[ks & 1]);
+      if (ks + 1 < KS) {
+        const u32x4 w = kr[((ks + 1) >> 1) % (KD / 2)];
+        kb = ((ks + 1) & 1) ? e4m3x8_to_bf16(w[2], w[3]) : e4m3x8_to_bf16(w[0], w[1]);
+      }
+      if ((ks & 1) && (ks >> 1) + KD / 2 < KS / 2) kload((ks >> 1) + KD / 2);
+    }
+  } else {
+    const int offE = ((g4) ^ fz) * 16;
+    const int offO = ((4 | g4) ^ fz) * 16;
+    bf16x8 kr[KD];
+    auto kload = [&](int ks) {
+      kr[ks % KD] = *(const DCP_LDS bf16x8*)(kp + (ks >> 1) * 128 + ((ks & 1) ? offO : offE));
+    };
+#pragma unroll
+    for (int ks = 0; ks < KD; ++ks) kload(ks);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      if ((ks & 1) == 0 && ks / 2 < DMA_N) copy_part<FP8>(nxt, ks / 2, goff, grow);
+      sc[ks & 1] = mfma_16x16x32(kr[ks % KD], qo.f[ks], sc[ks & 1]);
+      if (ks + KD < KS) kload(ks + KD);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
   // V^T operands of the value contraction: issued now, so their LDS latency
-  // overlaps the softmax and the probability exchange.
-  const int rowa = 4 * g4 + (r16 >> 2);
-  const int fa = swz(rowa);
-  const int hbit = (r16 & 3) >> 1;
-  const int byte = (r16 & 1) * 8;
-  const DCP_LDS char* va = st + rowa * ROW + byte + th * (VB / 2 / 4) * 128;
-  int voff[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) voff[q] = (((2 * q) | hbit) ^ fa) * 16;
+  // overlaps the softmax and the probability exchange.  k-slot i < 4 of lane
+  // group g4 is token 4*g4 + i, slot 4 + i token 16 + 4*g4 + i.
   constexpr int VD = 8;
-  i16x4 vlo[VD], vhi[VD];
+  i16x4 vlo[FP8 ? 1 : VD], vhi[FP8 ? 1 : VD];
+  uint2 v8r[FP8 ? VD : 1];
+  int voff[4];
+  const DCP_LDS char* va;
+  if constexpr (FP8) {
+    // lanes 2k, 2k + 1 of the group point at row k's 16-byte column block
+    const int k = r16 >> 1;
+    const int rowv = k < 4 ? 4 * g4 + k : 16 + 4 * g4 + (k - 4);
+    const int fv = swz<FP8>(rowv);
+    va = st + rowv * ROW + (r16 & 1) * 8 + th * (VB / 2) * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) voff[q] = (q ^ fv) * 16;
+  } else {
+    const int rowa = 4 * g4 + (r16 >> 2);
+    const int fa = swz<FP8>(rowa);
+    const int hbit = (r16 & 3) >> 1;
+    const int byte = (r16 & 1) * 8;
+    va = st + rowa * ROW + byte + th * (VB / 2 / 4) * 128;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) voff[q] = (((2 * q) | hbit) ^ fa) * 16;
+  }
   auto vload = [&](int cb) {
-    const DCP_LDS char* p0 = va + (cb >> 2) * 128 + voff[cb & 3];
-    vlo[cb % VD] = lds_read_tr16(p0);
-    vhi[cb % VD] = lds_read_tr16(p0 + 16 * ROW);
+    if constexpr (FP8) {
+      v8r[cb % VD] = lds_read_tr8(va + (cb >> 2) * 64 + voff[cb & 3]);
+    } else {
+      const DCP_LDS char* p0 = va + (cb >> 2) * 128 + voff[cb & 3];
+      vlo[cb % VD] = lds_read_tr16(p0);
+      vhi[cb % VD] = lds_read_tr16(p0 + 16 * ROW);
+    }
   };
   if constexpr (MODE == FULL) {
 #pragma unroll
@@ -316,7 +469,7 @@ __device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int tok0, i
   wait_lgkm0();
   barrier();
   // P^T operand over the 32 tokens: k-slots 0..3 hold tokens 4*g4 + i (half 0),
-  // slots 4..7 tokens 16 + 4*g4 + i (half 1), matching the V^T reads below.
+  // slots 4..7 tokens 16 + 4*g4 + i (half 1), matching the V^T reads.
   bf16x8 pt;
   {
     const bf16x4 oth = __builtin_bit_cast(bf16x4, xc.p[hq][th ^ 1][lane]);
@@ -327,13 +480,25 @@ __device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int tok0, i
 
   // ---- values O^T[col][head] += V^T[col][tok] . P^T[tok][head] for this wave's
   // 256 columns; V^T operands stream through a window of VD column blocks.
+  if constexpr (FP8) {
+    // each block's operand is converted while the previous block's MFMA runs
+    bf16x8 v8 = e4m3x8_to_bf16(v8r[0].x, v8r[0].y);
 #pragma unroll
-  for (int cb = 0; cb < VB / 2; ++cb) {
-    __builtin_amdgcn_sched_barrier(0);
-    const bf16x8 v8 = __builtin_bit_cast(
-        bf16x8, __builtin_shufflevector(vlo[cb % VD], vhi[cb % VD], 0, 1, 2, 3, 4, 5, 6, 7));
-    acc[cb] = mfma_16x16x32(v8, pt, acc[cb]);
-    if (cb + VD < VB / 2) vload(cb + VD);
+    for (int cb = 0; cb < VB / 2; ++cb) {
+      __builtin_amdgcn_sched_barrier(0);
+      acc[cb] = mfma_16x16x32(v8, pt, acc[cb]);
+      if (cb + 1 < VB / 2) v8 = e4m3x8_to_bf16(v8r[(cb + 1) % VD].x, v8r[(cb + 1) % VD].y);
+      if (cb + VD < VB / 2) vload(cb + VD);
+    }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < VB / 2; ++cb) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 v8 =
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(vlo[cb % VD], vhi[cb % VD], 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[cb] = mfma_16x16x32(v8, pt, acc[cb]);
+      if (cb + VD < VB / 2) vload(cb + VD);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -341,9 +506,11 @@ __device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int tok0, i
 // Runs the segment [t0, t1) of request b (tiles of the request).  FULL returns
 // true when the fixed softmax reference overflowed (nothing written then);
 // MAXIMUM stores the pair maximum of each head's scores in mref.
-template <int MODE>
+template <bool FP8, int MODE>
 __device__ __attribute__((always_inline)) inline bool run_segment(
-    const MlaArgs& a, Smem& sm, int b, int t0, int t1, int ntiles_b, int g, bool preset, float& mref) {
+    const MlaArgs& a, Smem<FP8>& sm, int b, int t0, int t1, int ntiles_b, int g, bool preset, float& mref) {
+  using F = Fmt<FP8>;
+  constexpr int NST = F::NST, DMA_N = F::DMA_N, CPT = F::CPT, CPR = F::CPR, ROW = F::ROW, STAGE = F::STAGE;
   const SplitArgs& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int heads = a.heads;
@@ -363,20 +530,14 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
     const int slot = min(i * NWAVE + wave, CPT - 1) * 64 + lane;
     const int r = slot / CPR, ch = slot % CPR;
     grow[i] = r;
-    goff[i] = r * ROW + ((ch ^ swz(r)) * 16);
+    goff[i] = r * ROW + ((ch ^ swz<FP8>(r)) * 16);
   }
 
   // q of this wave's 16 heads; heads past the request's count read as 0
   // (their results are computed and dropped)
-  bf16x8 qf[KS];
-  if (head < heads) {
-    const bf16x8* qp = (const bf16x8*)(a.q + ((int64_t)b * heads + head) * DK + 8 * g4);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = qp[4 * ks];
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16x8{};
-  }
+  QOps qo;
+  if (head < heads) load_q<FP8>(a.q + ((int64_t)b * heads + head) * DK, g4, qo);
+  else zero_q(qo);
   f32x4 acc[VB / 2];
 #pragma unroll
   for (int cb = 0; cb < VB / 2; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -397,14 +558,13 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
   barrier();
   // q has arrived (vmcnt 0); tie it here so the compiler places no wait for it
   // inside the tile loop, where it would drain the copy prefetch.
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(qf[ks]));
+  tie_q(qo);
   plan_prefetch(pl, sm);
 
-  copy_all(plan_next(a, trow, sm, pl, tiles, true), goff, grow);
+  copy_all<FP8>(plan_next(a, trow, sm, pl, tiles, true), goff, grow);
 #pragma unroll
   for (int j = 1; j < NST - 1; ++j)
-    if (n > j) copy_all(plan_next(a, trow, sm, pl, tiles + j * STAGE, true), goff, grow);
+    if (n > j) copy_all<FP8>(plan_next(a, trow, sm, pl, tiles + j * STAGE, true), goff, grow);
   // copy instructions this wave issues per tile: DMA_N, or one less where the
   // last round of slots does not reach this wave
   const bool full_round = uni(wave) + (DMA_N - 1) * NWAVE < CPT;
@@ -412,26 +572,19 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
     const int k = t0 + i;
     const int rem = n - 1 - i;
     // copies issued after tile k: those of min(NST - 2, rem) tiles
-    if (full_round) {
-      if (NST >= 4 && rem >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * DMA_N>();
-      else if (NST >= 3 && rem >= 1) wait_vmcnt<DMA_N>();
-      else wait_vmcnt<0>();
-    } else {
-      if (NST >= 4 && rem >= 2) wait_vmcnt<(NST >= 4 ? 2 : 0) * (DMA_N - 1)>();
-      else if (NST >= 3 && rem >= 1) wait_vmcnt<DMA_N - 1>();
-      else wait_vmcnt<0>();
-    }
+    if (full_round) wait_tiles<NST - 2, DMA_N>(rem);
+    else wait_tiles<NST - 2, DMA_N - 1>(rem);
     barrier();
     DCP_LDS char* cur = tiles + (i % NST) * STAGE;
     const int valid = lr - k * TILE;
     if (valid < TILE) {  // last tile of the request: clear rows past the end
-      zero_tail(cur, valid);
+      zero_tail<FP8>(cur, valid);
       wait_lgkm0();
       barrier();
     }
     const TileCopy nxt = plan_next(a, trow, sm, pl, tiles + ((i + NST - 1) % NST) * STAGE, i + NST - 1 < n);
-    compute_tile<MODE>(cur, k * TILE, lr, i == 0, preset, qf, acc, m, l, s.c, thr, ovf, sm.xc, th, hq, nxt, goff,
-                       grow);
+    compute_tile<FP8, MODE>(cur, k * TILE, lr, i == 0, preset, qo, acc, m, l, s.c, thr, ovf, sm.xc, th, hq, nxt,
+                            goff, grow);
   }
   if constexpr (MODE == MAXIMUM) {
     if (g4 == 0) sm.xc.mx[hq][th][r16] = m;
@@ -465,7 +618,8 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
     const int col = th * (R / 2) + 4 * g4;
     if (t0 == 0 && t1 == ntiles_b) {
       // the whole request is in this workgroup: write the final result
-      const float inv = 1.f / lt;
+      // an fp8 cache's values are vscale times the decoded codes
+      const float inv = FP8 ? a.vscale / lt : 1.f / lt;
       float* dst = s.out + ((size_t)b * heads + head) * R + col;
 #pragma unroll
       for (int cb = 0; cb < VB / 2; ++cb) *(f32x4*)(dst + 16 * cb) = acc[cb] * inv;
@@ -474,7 +628,7 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
       const int slot = g + b;
       float* dst = s.ws_o + ((size_t)slot * heads + head) * R + col;
 #pragma unroll
-      for (int cb = 0; cb < VB / 2; ++cb) *(f32x4*)(dst + 16 * cb) = acc[cb];
+      for (int cb = 0; cb < VB / 2; ++cb) *(f32x4*)(dst + 16 * cb) = FP8 ? acc[cb] * a.vscale : acc[cb];
       if (th == 0 && g4 == 0) {
         float* ml = s.ws_ml + ((size_t)slot * heads + head) * 2;
         ml[0] = m;
@@ -485,8 +639,9 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
   return false;
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(1024))) Smem sm;
+  __shared__ __attribute__((aligned(1024))) Smem<FP8> sm;
   const SplitArgs& s = a.s;
   const int tid = threadIdx.x;
   const int g = blockIdx.x;
@@ -511,8 +666,8 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
       float mref = 0.f;
       bool preset = false;
       for (int pass = 0; pass < 2; ++pass) {
-        if (!run_segment<FULL>(a, sm, b, st.t0, st.t1, st.ntiles, g, preset, mref)) break;
-        run_segment<MAXIMUM>(a, sm, b, st.t0, st.t1, st.ntiles, g, false, mref);
+        if (!run_segment<FP8, FULL>(a, sm, b, st.t0, st.t1, st.ntiles, g, preset, mref)) break;
+        run_segment<FP8, MAXIMUM>(a, sm, b, st.t0, st.t1, st.ntiles, g, false, mref);
         preset = true;
       }
     }
@@ -536,7 +691,8 @@ __global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(MlaArgs a, int b
 
 hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream) {
   if (a.s.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(mla::partial_kernel, dim3(a.s.G), dim3(mla::THREADS), 0, stream, a);
+  if (a.fp8) hipLaunchKernelGGL(mla::partial_kernel<true>, dim3(a.s.G), dim3(mla::THREADS), 0, stream, a);
+  else hipLaunchKernelGGL(mla::partial_kernel<false>, dim3(a.s.G), dim3(mla::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const ReducePlan rp = reduce_plan(a.s.batch, a.heads, a.s.G, mla::RED_COL_PARTS);

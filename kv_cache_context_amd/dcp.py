@@ -29,7 +29,7 @@ DCP_LAYOUT_CONTIGUOUS = 1
 
 # every symbol the header declares
 EXPORTED = (
-    "dcp_mla_workspace_bytes", "dcp_mla_decode_partial",
+    "dcp_mla_workspace_bytes", "dcp_mla_decode_partial", "dcp_mla_decode_partial_fp8",
     "dcp_gqa_workspace_bytes", "dcp_gqa_decode_partial",
     "dcp_combine", "dcp_combine_vproj_gate", "dcp_status_string", "dcp_last_hip_error", "dcp_abi_version",
 )
@@ -86,6 +86,9 @@ def lib() -> ctypes.CDLL:
     L.dcp_mla_decode_partial.argtypes = [ctypes.POINTER(dcp_mla_params), _P, _P, _P, _P, _P, _P, _P,
                                          ctypes.c_size_t, _P]
     L.dcp_mla_decode_partial.restype = ctypes.c_int
+    L.dcp_mla_decode_partial_fp8.argtypes = [ctypes.POINTER(dcp_mla_params), _P, _P, ctypes.c_float, _P, _P, _P,
+                                             _P, _P, ctypes.c_size_t, _P]
+    L.dcp_mla_decode_partial_fp8.restype = ctypes.c_int
     L.dcp_gqa_workspace_bytes.argtypes = [ctypes.POINTER(dcp_gqa_params)]
     L.dcp_gqa_workspace_bytes.restype = ctypes.c_size_t
     L.dcp_gqa_decode_partial.argtypes = [ctypes.POINTER(dcp_gqa_params), _P, _P, _P, _P, _P, _P, _P, _P,
@@ -134,6 +137,13 @@ def dcp_mla_decode_partial(p: dcp_mla_params, q: int, kv_cache: int, block_table
                            out: int, lse: int, workspace: int, workspace_bytes: int, stream: int) -> int:
     return int(lib().dcp_mla_decode_partial(ctypes.byref(p), q, kv_cache, block_table, seq_lens, out, lse,
                                             workspace, workspace_bytes, stream))
+
+
+def dcp_mla_decode_partial_fp8(p: dcp_mla_params, q: int, kv_cache: int, kv_scale: float, block_table: int,
+                               seq_lens: int, out: int, lse: int, workspace: int, workspace_bytes: int,
+                               stream: int) -> int:
+    return int(lib().dcp_mla_decode_partial_fp8(ctypes.byref(p), q, kv_cache, kv_scale, block_table, seq_lens,
+                                                out, lse, workspace, workspace_bytes, stream))
 
 
 def dcp_gqa_decode_partial(p: dcp_gqa_params, q: int, k_cache: int, v_cache: int, block_table: int,

@@ -65,9 +65,11 @@ def gqa_workspace(p: _abi.dcp_gqa_params, device) -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def dcp_mla_decode_partial(p, q, kv_cache, block_table, seq_lens, out, lse, workspace, stream=None) -> None:
+def _mla_check(p, q, kv_cache, kv_dtypes, block_table, seq_lens, out, lse):
     _req(q, torch.bfloat16, 3, "q")
-    _req(kv_cache, torch.bfloat16, 3, "kv_cache")
+    if kv_cache.dtype not in kv_dtypes:
+        raise TypeError(f"kv_cache: expected one of {kv_dtypes}, got {kv_cache.dtype}")
+    _req(kv_cache, kv_cache.dtype, 3, "kv_cache")
     _req(block_table, torch.int32, 2, "block_table")
     _req(seq_lens, torch.int32, 1, "seq_lens")
     _req(out, torch.float32, 3, "out")
@@ -83,10 +85,26 @@ def dcp_mla_decode_partial(p, q, kv_cache, block_table, seq_lens, out, lse, work
         raise ValueError("seq_lens shape")
     if tuple(out.shape) != (_rows(p), p.num_heads, p.kv_lora_rank) or tuple(lse.shape) != (_rows(p), p.num_heads):
         raise ValueError("out/lse shape")
+
+
+def dcp_mla_decode_partial(p, q, kv_cache, block_table, seq_lens, out, lse, workspace, stream=None) -> None:
+    _mla_check(p, q, kv_cache, (torch.bfloat16,), block_table, seq_lens, out, lse)
     _abi.check(_abi.dcp_mla_decode_partial(p, q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
                                            seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                            _stream(stream)), "dcp_mla_decode_partial")
+
+
+def dcp_mla_decode_partial_fp8(p, q, kv_cache, kv_scale, block_table, seq_lens, out, lse, workspace,
+                               stream=None) -> None:
+    """MLA partial over an fp8 cache: kv_cache holds E4M3 codes (torch.float8_e4m3fn
+    or uint8) [num_blocks, block_size, 576]; kv_scale dequantizes the whole cache."""
+    _mla_check(p, q, kv_cache, (torch.float8_e4m3fn, torch.uint8), block_table, seq_lens, out, lse)
+    _abi.check(_abi.dcp_mla_decode_partial_fp8(p, q.data_ptr(), kv_cache.data_ptr(), float(kv_scale),
+                                               block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                                               lse.data_ptr(), workspace.data_ptr(),
+                                               workspace.numel() * workspace.element_size(), _stream(stream)),
+               "dcp_mla_decode_partial_fp8")
 
 
 def dcp_gqa_decode_partial(p, q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace,

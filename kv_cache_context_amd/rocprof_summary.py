@@ -35,10 +35,14 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {
     "mla": ["csrc/mla_partial.hip", "csrc/dcp_device.hpp", "csrc/dcp_split.hpp", "csrc/dcp_internal.hpp", "build.py"],
+    "mla8": ["csrc/mla_partial.hip", "csrc/dcp_device.hpp", "csrc/dcp_split.hpp", "csrc/dcp_internal.hpp", "build.py"],
     "gqa": ["csrc/gqa_partial.hip", "csrc/dcp_device.hpp", "csrc/dcp_split.hpp", "csrc/dcp_internal.hpp", "build.py"],
     "combine": ["csrc/combine.hip", "csrc/dcp_device.hpp", "csrc/dcp_internal.hpp", "build.py"],
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+# kernel-name substring of each kind's partial kernel in traces
+PARTIAL_KERNEL = {"mla": "mla::partial_kernel<false>", "mla8": "mla::partial_kernel<true>",
+                  "gqa": "gqa::partial_kernel"}
 
 
 def source_hash(kind: str) -> str:
@@ -118,7 +122,7 @@ def report(prof: str, wl: str, kind: str, bench_args: str | None = None) -> tupl
     fetch = os.path.join(prof, f"{wl}_FETCH_SIZE", "p_counter_collection.csv")
     write = os.path.join(prof, f"{wl}_WRITE_SIZE", "p_counter_collection.csv")
     if os.path.exists(fetch) and os.path.exists(write):
-        t = traffic(fetch, write, f"{kind}::partial_kernel", CAL_COPY_BYTES)
+        t = traffic(fetch, write, PARTIAL_KERNEL[kind], CAL_COPY_BYTES)
         lines += ["HBM traffic of partial_kernel from two counter runs (KiB per dispatch, scaled by the",
                   "counter's reading for a 1 GiB device copy in the same process):", "", "```", pmc_cmd, "```", "",
                   "| counter | KiB/dispatch | copy reads KiB | scale | bytes/launch |", "|---|---|---|---|---|"]

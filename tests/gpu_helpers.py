@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads as W
-from workloads.device import bf16_tensor, int32_tensor
+from workloads.device import bf16_tensor, fp8_tensor, int32_tensor
 from kv_cache_context_amd import ops
 
 # Parity bar: per (request, head) row, max|o - o_ref| / max|o_ref| <= 1e-2
@@ -44,7 +44,7 @@ class ShardRun:
                       num_blocks=sc.num_blocks, shard_rank=r, num_shards=w.num_shards, layout=w.layout,
                       max_seq_len_hint=max(1, case.max_seq_len), softmax_scale=w.scale)
         if w.kind == "mla":
-            self.kv = bf16_tensor(sc.pools[0], dev)
+            self.kv = bf16_tensor(sc.pools[0], dev) if case.kv_fp8_scale is None else fp8_tensor(sc.pools[0], dev)
             self.p = ops.mla_params(batch=b, num_heads=w.heads, **common)
             self.ws = workspace if workspace is not None else ops.mla_workspace(self.p, dev)
         else:
@@ -59,7 +59,10 @@ class ShardRun:
     def run(self, out=None, lse=None):
         out = self.out if out is None else out
         lse = self.lse if lse is None else lse
-        if self.case.w.kind == "mla":
+        if self.case.w.kind == "mla" and self.case.kv_fp8_scale is not None:
+            ops.dcp_mla_decode_partial_fp8(self.p, self.q, self.kv, self.case.kv_fp8_scale, self.table,
+                                           self.seq_lens, out, lse, self.ws, self.stream)
+        elif self.case.w.kind == "mla":
             ops.dcp_mla_decode_partial(self.p, self.q, self.kv, self.table, self.seq_lens, out, lse, self.ws,
                                        self.stream)
         else:
@@ -87,6 +90,9 @@ def oracle_rows(case: W.Case, b: int, heads, r: int | None):
         pos = np.arange(L)
     else:
         pos = oracle.shard_positions(L, w.num_shards, r, w.layout)
+    if w.kind == "mla" and case.kv_fp8_scale is not None:
+        bits = case.rows_at(b, pos)[0] if len(pos) else np.zeros((0, w.dk), np.uint8)
+        return oracle.mla_attention_fp8(q, bits, case.kv_fp8_scale, w.scale, w.kv_lora_rank)
     if w.kind == "mla":
         kv = oracle.widen_bf16(case.rows_at(b, pos)[0]) if len(pos) else np.zeros((0, w.dk))
         return oracle.mla_attention(q, kv, w.scale, w.kv_lora_rank)

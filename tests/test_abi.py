@@ -94,6 +94,20 @@ def test_mla_pointer_and_workspace_checks():
     assert dcp.dcp_mla_workspace_bytes(mla(max_seq_len_hint=100)) == need
 
 
+def test_mla_fp8_validation():
+    """The fp8 entry point checks its scale first, then everything the bf16 one does."""
+    p = mla()
+    need = dcp.dcp_mla_workspace_bytes(p)
+    f = dcp.dcp_mla_decode_partial_fp8
+    for bad in (0.0, -1.0, float("nan"), float("inf"), 1e-38):
+        assert f(p, FAKE, FAKE, bad, FAKE, FAKE, FAKE, FAKE, FAKE, need, 0) == 1, bad
+    assert f(mla(num_heads=60), FAKE, FAKE, 0.5, FAKE, FAKE, FAKE, FAKE, FAKE, need, 0) == 2
+    assert f(p, FAKE, 0, 0.5, FAKE, FAKE, FAKE, FAKE, FAKE, need, 0) == 1
+    assert f(p, FAKE, FAKE + 8, 0.5, FAKE, FAKE, FAKE, FAKE, FAKE, need, 0) == 1   # misaligned cache
+    assert f(p, FAKE, FAKE, 0.5, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 0) == 3
+    assert f(mla(batch=0), 0, 0, 0.5, 0, 0, 0, 0, 0, 0, 0) == 0
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(num_q_heads=60), 1), (dict(num_kv_heads=0), 1), (dict(shard_rank=4), 1), (dict(batch=-3), 1),
     (dict(head_dim=64), 2), (dict(num_kv_heads=2, num_q_heads=16), 2), (dict(num_q_heads=256, num_kv_heads=8), 2),
