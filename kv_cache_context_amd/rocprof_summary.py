@@ -91,12 +91,14 @@ CAL_COPY_BYTES = 1 << 30
 
 
 def report(prof: str, wl: str, kind: str, bench_args: str | None = None) -> tuple[str, dict | None]:
-    if bench_args is None:
-        bench_args = f"--workload {wl}" + ("" if wl == "c1" else " --no-cpu-baseline")
+    """bench_args: the bench arguments of the runs (default --workload <wl>); the kernel-trace run adds
+    --no-cpu-baseline except for c1, the counter runs their own short-run flags."""
+    base = bench_args if bench_args is not None else f"--workload {wl}"
+    kt_args = base + ("" if base == "--workload c1" else " --no-cpu-baseline")
     kt_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {prof}/{wl} -o kt -- "
-              f"python -u bench.py {bench_args}".rstrip())
+              f"python -u bench.py {kt_args}")
     pmc_cmd = (f"rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d {prof}/{wl}_<counter> -o p -- "
-               f"python -u bench.py --workload {wl} --steps 5 --warmup 1 --no-cpu-baseline --calibration-copy")
+               f"python -u bench.py {base} --steps 5 --warmup 1 --no-cpu-baseline --calibration-copy")
     bench = None
     logp = os.path.join(prof, f"{wl}_kt.log")
     if os.path.exists(logp):
