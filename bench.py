@@ -357,7 +357,7 @@ def main():
     step_gbs = (alg_partial + alg_comb) / (ms_per_step * 1e-3) / 1e9
 
     res = {
-        "metric": "us/decode step + achieved HBM GB/s (% peak), shard-local attn + combine",
+        "metric": "\u00b5s/decode step + achieved HBM GB/s (% peak), shard-local MLA attn + combine",
         "value": round(ms_per_step * 1e3, 3),
         "unit": "us/step",
         "n_gpus": 1,
