@@ -288,7 +288,7 @@ __device__ __forceinline__ uint2 lds_read_tr8(const DCP_LDS char* p) {
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 // This lane's query operands for the 18 k-steps of the score contraction of one
-// head.  bf16 cache: step ks holds latent k = 32 ks + 8 g4 + 0..7.  fp8 cache:
+// head (filled from the staged rows by load_q_lds).  bf16 cache: step ks holds latent k = 32 ks + 8 g4 + 0..7.  fp8 cache:
 // steps 2j and 2j + 1 hold k = 64 j + 16 g4 + 0..7 and + 8..15 (the k order in
 // which one 16-byte chunk of an fp8 row feeds two steps).  The sum over k does
 // not depend on the order.
@@ -296,21 +296,6 @@ struct QOps {
   bf16x8 f[KS];
 };
 
-template <bool FP8>
-__device__ __forceinline__ void load_q(const uint16_t* qrow, int g4, QOps& q) {
-  if constexpr (FP8) {
-    const uint16_t* qp = qrow + 16 * g4;
-#pragma unroll
-    for (int j = 0; j < KS / 2; ++j) {
-      q.f[2 * j] = *(const bf16x8*)(qp + 64 * j);
-      q.f[2 * j + 1] = *(const bf16x8*)(qp + 64 * j + 8);
-    }
-  } else {
-    const bf16x8* qp = (const bf16x8*)(qrow + 8 * g4);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) q.f[ks] = qp[4 * ks];
-  }
-}
 __device__ __forceinline__ void zero_q(QOps& q) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) q.f[ks] = bf16x8{};
@@ -318,6 +303,31 @@ __device__ __forceinline__ void zero_q(QOps& q) {
 __device__ __forceinline__ void tie_q(QOps& q) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(q.f[ks]));
+}
+
+// q of a request's heads, staged in LDS: copies of 1 KiB of the [heads][576]
+// bf16 block (rows of 1152 B, contiguous in HBM and in LDS), spread over the
+// waves.  A per-lane load of the MFMA operand layout touches 16 head rows per
+// instruction; the staged copy reads q in whole contiguous KiBs.
+__device__ __forceinline__ void stage_q(const uint16_t* qreq, int heads, DCP_LDS char* qs) {
+  const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int nq = heads * (DK * 2) / 1024;  // exact: heads is a multiple of 16
+  for (int j = wave; j < nq; j += NWAVE) dma16((const char*)qreq + j * 1024 + lane * 16, qs + j * 1024);
+}
+
+// This lane's q operands from the staged rows (the layouts of QOps).
+template <bool FP8>
+__device__ __forceinline__ void load_q_lds(const DCP_LDS char* qrow, int g4, QOps& q) {
+  if constexpr (FP8) {
+#pragma unroll
+    for (int j = 0; j < KS / 2; ++j) {
+      q.f[2 * j] = *(const DCP_LDS bf16x8*)(qrow + 128 * j + 32 * g4);
+      q.f[2 * j + 1] = *(const DCP_LDS bf16x8*)(qrow + 128 * j + 32 * g4 + 16);
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) q.f[ks] = *(const DCP_LDS bf16x8*)(qrow + 64 * ks + 16 * g4);
+  }
 }
 
 // One 32-token tile: this wave's scores over its 16 tokens for its 16 heads,
@@ -536,8 +546,6 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
   // q of this wave's 16 heads; heads past the request's count read as 0
   // (their results are computed and dropped)
   QOps qo;
-  if (head < heads) load_q<FP8>(a.q + ((int64_t)b * heads + head) * DK, g4, qo);
-  else zero_q(qo);
   f32x4 acc[VB / 2];
 #pragma unroll
   for (int cb = 0; cb < VB / 2; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -552,22 +560,40 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
   pl.pg_hi = uni(min(s.max_blocks, (min(t1 * TILE, lr) - 1) / s.block_size + 1));
   pl.win.lo = pl.pg;
   pl.win.end = min(pl.pg_hi, pl.pg + TBL);
-  load_window(a, trow, sm, pl.pg, pl.pg_hi);  // in flight together with the q loads
+  load_window(a, trow, sm, pl.pg, pl.pg_hi);
   wait_vmcnt<0>();
   wait_lgkm0();
   barrier();
-  // q has arrived (vmcnt 0); tie it here so the compiler places no wait for it
-  // inside the tile loop, where it would drain the copy prefetch.
-  tie_q(qo);
   plan_prefetch(pl, sm);
 
-  copy_all<FP8>(plan_next(a, trow, sm, pl, tiles, true), goff, grow);
-#pragma unroll
-  for (int j = 1; j < NST - 1; ++j)
-    if (n > j) copy_all<FP8>(plan_next(a, trow, sm, pl, tiles + j * STAGE, true), goff, grow);
+  // q goes to the last QST stages while the first A tiles' copies go out, so
+  // the two travel together; then q is read into registers, its stages are
+  // released and the remaining tiles of the ring are requested.
+  constexpr int QST = (64 * DK * 2 + STAGE - 1) / STAGE;  // stages holding up to 64 heads of q
+  constexpr int A = NST - QST;                            // tiles requested before q is read
+  static_assert(A >= 1 && A <= NST - 1, "q staging");
+  DCP_LDS char* qs = tiles + A * STAGE;
+  stage_q(a.q + (int64_t)b * heads * DK, heads, qs);
   // copy instructions this wave issues per tile: DMA_N, or one less where the
   // last round of slots does not reach this wave
   const bool full_round = uni(wave) + (DMA_N - 1) * NWAVE < CPT;
+#pragma unroll
+  for (int j = 0; j < A; ++j)
+    if (n > j) copy_all<FP8>(plan_next(a, trow, sm, pl, tiles + j * STAGE, true), goff, grow);
+  // the q copies are older than the tiles' copies issued since
+  if (full_round) wait_tiles<A, DMA_N>(n);
+  else wait_tiles<A, DMA_N - 1>(n);
+  barrier();
+  if (head < heads) load_q_lds<FP8>(qs + head * (DK * 2), g4, qo);
+  else zero_q(qo);
+  wait_lgkm0();
+  barrier();  // every wave has its q: the staging stages are free
+  // q is in registers (lgkmcnt 0); tie it here so the compiler places no wait
+  // for it inside the tile loop.
+  tie_q(qo);
+#pragma unroll
+  for (int j = A; j < NST - 1; ++j)
+    if (n > j) copy_all<FP8>(plan_next(a, trow, sm, pl, tiles + j * STAGE, true), goff, grow);
   for (int i = 0; i < n; ++i) {
     const int k = t0 + i;
     const int rem = n - 1 - i;
