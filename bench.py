@@ -323,7 +323,7 @@ def main():
         return g
 
     def timed_replay(g, reps=3):
-        best = None
+        times = []
         for _ in range(reps):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -332,9 +332,8 @@ def main():
                 g.replay()
                 e1.record(side)
             e1.synchronize()
-            t = e0.elapsed_time(e1)
-            best = t if best is None else min(best, t)
-        return best
+            times.append(e0.elapsed_time(e1))
+        return sorted(times)[len(times) // 2]  # median replay
 
     g_step = capture(step)
     g_part = capture(do_partials)
@@ -343,7 +342,7 @@ def main():
     with torch.cuda.stream(side):
         g_step.replay()  # warm the graph once
     torch.cuda.synchronize()
-    total_ms = timed_replay(g_step, reps=1)
+    total_ms = timed_replay(g_step)
     ms_per_step = total_ms / args.steps
     part_ms = timed_replay(g_part)
     comb_ms = timed_replay(g_comb)
@@ -379,7 +378,7 @@ def main():
         "combine_us": round(comb_mean, 3),
         "epilogue": "dcp_combine_vproj_gate" if args.epilogue == "vproj" else "dcp_combine",
         "epilogue_gbps": round(alg_comb / (comb_mean * 1e-6) / 1e9, 1),
-        "timing": "K steps captured in one HIP graph, replayed; HIP events around the replay",
+        "timing": "K steps captured in one HIP graph; HIP events around each of 3 replays, median replay",
         "mfma_tflops": round(flops / (part_mean * 1e-6) / 1e12, 2),
         "mfma_frac": round(flops / (part_mean * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "kernel": f"dcp_{w.kind}_decode_partial" + ("_fp8" if fp8 else ""),

@@ -73,7 +73,7 @@ dcp::SplitArgs split_args(int batch, int block_size, int max_blocks, int num_blo
   s.seq_lens = seq_lens;
   s.ws_meta = (int32_t*)((char*)ws + wl.meta_off);
   s.ws_ml = (float*)((char*)ws + wl.ml_off);
-  s.ws_o = (float*)((char*)ws + wl.o_off);
+  s.ws_o = (char*)ws + wl.o_off;
   s.out = out;
   s.lse = lse;
   s.batch = batch;
@@ -150,7 +150,7 @@ dcp_status mla_partial(const dcp_mla_params* p, const void* q, const void* kv_ca
       !aligned(seq_lens, 4) || !aligned(lse, 4))
     return DCP_ERR_INVALID_ARGUMENT;
   const int rows = rows_of(p->batch, p->q_len);
-  const dcp::WsLayout wl = dcp::ws_layout(rows, p->num_heads, 512);
+  const dcp::WsLayout wl = dcp::ws_layout(rows, p->num_heads, 512, 2);
   if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
   hipError_t herr = hipSuccess;
   const int cus = device_cus(&herr);
@@ -194,7 +194,7 @@ const char* dcp_status_string(dcp_status s) {
 
 size_t dcp_mla_workspace_bytes(const dcp_mla_params* p) {
   if (mla_check(p) != DCP_OK) return 0;
-  return dcp::ws_layout(rows_of(p->batch, p->q_len), p->num_heads, 512).total;
+  return dcp::ws_layout(rows_of(p->batch, p->q_len), p->num_heads, 512, 2).total;
 }
 
 dcp_status dcp_mla_decode_partial(const dcp_mla_params* p, const void* q, const void* kv_cache,
@@ -215,7 +215,7 @@ dcp_status dcp_mla_decode_partial_fp8(const dcp_mla_params* p, const void* q, co
 
 size_t dcp_gqa_workspace_bytes(const dcp_gqa_params* p) {
   if (gqa_check(p) != DCP_OK) return 0;
-  return dcp::ws_layout(rows_of(p->batch, p->q_len), p->num_q_heads, 128).total;
+  return dcp::ws_layout(rows_of(p->batch, p->q_len), p->num_q_heads, 128, 4).total;
 }
 
 dcp_status dcp_gqa_decode_partial(const dcp_gqa_params* p, const void* q, const void* k_cache,
@@ -231,7 +231,7 @@ dcp_status dcp_gqa_decode_partial(const dcp_gqa_params* p, const void* q, const 
       !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(lse, 4))
     return DCP_ERR_INVALID_ARGUMENT;
   const int rows = rows_of(p->batch, p->q_len);
-  const dcp::WsLayout wl = dcp::ws_layout(rows, p->num_q_heads, 128);
+  const dcp::WsLayout wl = dcp::ws_layout(rows, p->num_q_heads, 128, 4);
   if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
   hipError_t herr = hipSuccess;
   const int cus = device_cus(&herr);

@@ -16,19 +16,21 @@ constexpr int kMaxBatch = 2048;
 // Workspace layout of a partial call (all offsets 256-byte aligned):
 //   meta  int32 [kMaxBatch + 2]: [0] = split WGs used, [1 + b] = tile prefix sum
 //   ml    fp32  [slots][heads][2]: running max (raw score units) and softmax sum
-//   o     fp32  [slots][heads][dv]: unnormalized partial output
+//   o     [slots][heads][dv]: unnormalized partial output, fp32 (GQA) or bf16
+//         (MLA: one 64-head partial is 64 KiB instead of 128, halving the
+//         split traffic; see the partial kernel)
 // slots = kMaxSplitWGs + batch.
 struct WsLayout {
   size_t meta_off, ml_off, o_off, total;
 };
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline WsLayout ws_layout(int batch, int heads, int dv) {
+inline WsLayout ws_layout(int batch, int heads, int dv, size_t o_bytes) {
   WsLayout w;
   const size_t slots = (size_t)kMaxSplitWGs + (size_t)batch;
   w.meta_off = 0;
   w.ml_off = align256(sizeof(int32_t) * (kMaxBatch + 2));
   w.o_off = w.ml_off + align256(sizeof(float) * slots * heads * 2);
-  w.total = w.o_off + align256(sizeof(float) * slots * heads * dv);
+  w.total = w.o_off + align256(o_bytes * slots * heads * dv);
   return w;
 }
 
@@ -37,7 +39,7 @@ struct SplitArgs {
   const int32_t* seq_lens;
   int32_t* ws_meta;
   float* ws_ml;
-  float* ws_o;
+  void* ws_o;  // element type per kernel (fp32 or bf16)
   float* out;
   float* lse;
   int batch, block_size, max_blocks, num_blocks, rank, nshards, layout;

@@ -189,10 +189,36 @@ template <int N>
 struct FVec {
   float v[N];
 };
-template <int N>
-__device__ __forceinline__ FVec<N> load_cols(const float* p) {
+// N consecutive partial columns as fp32, from fp32 or bf16 (uint16_t bits)
+// storage.
+template <int N, typename T>
+__device__ __forceinline__ FVec<N> load_cols(const T* p) {
   FVec<N> r;
-  if constexpr (N % 4 == 0) {
+  if constexpr (sizeof(T) == 2) {
+    static_assert(N == 2 || N == 4 || N % 8 == 0, "bf16 column run");
+    uint32_t w[N / 2];
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+      for (int k = 0; k < N / 8; ++k) {
+        const uint4 x = *(const uint4*)(p + 8 * k);
+        w[4 * k] = x.x;
+        w[4 * k + 1] = x.y;
+        w[4 * k + 2] = x.z;
+        w[4 * k + 3] = x.w;
+      }
+    } else if constexpr (N == 4) {
+      const uint2 x = *(const uint2*)p;
+      w[0] = x.x;
+      w[1] = x.y;
+    } else {
+      w[0] = *(const uint32_t*)p;
+    }
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) {
+      r.v[2 * k] = __uint_as_float(w[k] << 16);
+      r.v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+  } else if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int k = 0; k < N / 4; ++k) {
       const float4 x = *(const float4*)(p + 4 * k);
@@ -231,8 +257,9 @@ struct ReduceSmem {
   float part[REDUCE_THREADS / 64][512];  // by-segments mapping: per-wave sums of a column part
 };
 
-// By heads: block (head group hg, request b).
-template <int DV>
+// By heads: block (head group hg, request b).  T: element type of the
+// workspace partials (float, or uint16_t holding bf16).
+template <int DV, typename T>
 __device__ __forceinline__ void reduce_by_heads(const SplitArgs& s, int heads, int b, int hg, ReduceSmem& sm) {
   constexpr int C = DV / 64;  // columns per lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -254,7 +281,7 @@ __device__ __forceinline__ void reduce_by_heads(const SplitArgs& s, int heads, i
   const size_t stride = (size_t)heads * DV;
   for (int j = wave; j < nh; j += REDUCE_THREADS / 64) {
     const int h = h0 + j;
-    const float* src = s.ws_o + ((size_t)(r.g0 + b) * heads + h) * DV + lane * C;
+    const T* src = (const T*)s.ws_o + ((size_t)(r.g0 + b) * heads + h) * DV + lane * C;
     const float* w = sm.w + j * kMaxSplitWGs;
     FVec<C> acc;
 #pragma unroll
@@ -263,14 +290,14 @@ __device__ __forceinline__ void reduce_by_heads(const SplitArgs& s, int heads, i
     for (; i + 4 <= r.nseg; i += 4) {
       FVec<C> x[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = load_cols<C>(src + (size_t)(i + u) * stride);
+      for (int u = 0; u < 4; ++u) x[u] = load_cols<C, T>(src + (size_t)(i + u) * stride);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int k = 0; k < C; ++k) acc.v[k] += w[i + u] * x[u].v[k];
     }
     for (; i < r.nseg; ++i) {
-      const FVec<C> x = load_cols<C>(src + (size_t)i * stride);
+      const FVec<C> x = load_cols<C, T>(src + (size_t)i * stride);
 #pragma unroll
       for (int k = 0; k < C; ++k) acc.v[k] += w[i] * x.v[k];
     }
@@ -283,7 +310,7 @@ __device__ __forceinline__ void reduce_by_heads(const SplitArgs& s, int heads, i
 }
 
 // By segments: block (column part cp of CP, head h, request b).
-template <int DV, int CP>
+template <int DV, int CP, typename T>
 __device__ __forceinline__ void reduce_by_segments(const SplitArgs& s, int heads, int b, int h, int cp,
                                                    ReduceSmem& sm) {
   constexpr int C = DV / CP / 64;  // columns per lane
@@ -304,7 +331,7 @@ __device__ __forceinline__ void reduce_by_segments(const SplitArgs& s, int heads
   }
   seg_weights(s, heads, b, r, h, 1, sm.w, sm.M, sm.L);
   const size_t stride = (size_t)heads * DV;
-  const float* src = s.ws_o + ((size_t)(r.g0 + b) * heads + h) * DV + col;
+  const T* src = (const T*)s.ws_o + ((size_t)(r.g0 + b) * heads + h) * DV + col;
   constexpr int NW = REDUCE_THREADS / 64;
   FVec<C> acc;
 #pragma unroll
@@ -314,14 +341,14 @@ __device__ __forceinline__ void reduce_by_segments(const SplitArgs& s, int heads
   for (; i + (U - 1) * NW < r.nseg; i += U * NW) {
     FVec<C> x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) x[u] = load_cols<C>(src + (size_t)(i + u * NW) * stride);
+    for (int u = 0; u < U; ++u) x[u] = load_cols<C, T>(src + (size_t)(i + u * NW) * stride);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int k = 0; k < C; ++k) acc.v[k] += sm.w[i + u * NW] * x[u].v[k];
   }
   for (; i < r.nseg; i += NW) {
-    const FVec<C> x = load_cols<C>(src + (size_t)i * stride);
+    const FVec<C> x = load_cols<C, T>(src + (size_t)i * stride);
 #pragma unroll
     for (int k = 0; k < C; ++k) acc.v[k] += sm.w[i] * x.v[k];
   }

@@ -270,7 +270,7 @@ __device__ __forceinline__ void run_segment(const GqaArgs& a, Smem& sm, int quad
       if (g4 == 0) s.lse[(size_t)b * a.hq + qh] = (m * s.c + __log2f(lt)) * kLn2;
     } else {
       const int slot = g + b;
-      float* dst = s.ws_o + ((size_t)slot * a.hq + qh) * D + 4 * g4;
+      float* dst = (float*)s.ws_o + ((size_t)slot * a.hq + qh) * D + 4 * g4;
 #pragma unroll
       for (int cb = 0; cb < VB; ++cb) *(f32x4*)(dst + 16 * cb) = acc[cb];
       if (g4 == 0) {
@@ -310,8 +310,8 @@ constexpr int RED_COL_PARTS = 1;  // column parts of the by-segments reduce
 
 __global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(GqaArgs a, int by_segments) {
   __shared__ ReduceSmem sm;
-  if (by_segments) reduce_by_segments<D, RED_COL_PARTS>(a.s, a.hq, blockIdx.z, blockIdx.y, blockIdx.x, sm);
-  else reduce_by_heads<D>(a.s, a.hq, blockIdx.y, blockIdx.x, sm);
+  if (by_segments) reduce_by_segments<D, RED_COL_PARTS, float>(a.s, a.hq, blockIdx.z, blockIdx.y, blockIdx.x, sm);
+  else reduce_by_heads<D, float>(a.s, a.hq, blockIdx.y, blockIdx.x, sm);
 }
 
 }  // namespace gqa

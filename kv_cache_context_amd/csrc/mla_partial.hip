@@ -28,7 +28,8 @@
 //    with V^T read straight from the row-major tile by ds_read_b64_tr_b16.
 //  * LDS rows are 1152 B; 16-byte chunks are XOR-swizzled per row so both the
 //    row-wise K reads and the transposing V reads hit distinct banks.
-//  * Split-K partials go to the workspace and a small kernel merges them.
+//  * Split-K partials go to the workspace (as bf16) and a small kernel merges
+//    them.
 //
 // fp8 latent cache (the Kimi K3 optimizations page serves with an fp8 KV
 // cache): rows hold 576 OCP E4M3 codes and one scale s dequantizes the whole
@@ -651,10 +652,18 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
       for (int cb = 0; cb < VB / 2; ++cb) *(f32x4*)(dst + 16 * cb) = acc[cb] * inv;
       if (th == 0 && g4 == 0) s.lse[(size_t)b * heads + head] = (m * s.c + __log2f(lt)) * kLn2;
     } else {
+      // split partials are stored as bf16, rounded to nearest even, which
+      // halves the split write and its read back.  Each element moves by at
+      // most 2^-9 of itself; as |o_i| <= l_i max|v| and the merge divides
+      // sum w_i o_i by sum w_i l_i, the merged output moves by at most
+      // 2^-9 max|v|.
       const int slot = g + b;
-      float* dst = s.ws_o + ((size_t)slot * heads + head) * R + col;
+      uint16_t* dst = (uint16_t*)s.ws_o + ((size_t)slot * heads + head) * R + col;
 #pragma unroll
-      for (int cb = 0; cb < VB / 2; ++cb) *(f32x4*)(dst + 16 * cb) = FP8 ? acc[cb] * a.vscale : acc[cb];
+      for (int cb = 0; cb < VB / 2; ++cb) {
+        const f32x4 v = FP8 ? acc[cb] * a.vscale : acc[cb];
+        *(uint2*)(dst + 16 * cb) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
       if (th == 0 && g4 == 0) {
         float* ml = s.ws_ml + ((size_t)slot * heads + head) * 2;
         ml[0] = m;
@@ -709,8 +718,8 @@ constexpr int RED_COL_PARTS = DCP_MLA_RED_COL_PARTS;  // column parts of the by-
 
 __global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(MlaArgs a, int by_segments) {
   __shared__ ReduceSmem sm;
-  if (by_segments) reduce_by_segments<R, RED_COL_PARTS>(a.s, a.heads, blockIdx.z, blockIdx.y, blockIdx.x, sm);
-  else reduce_by_heads<R>(a.s, a.heads, blockIdx.y, blockIdx.x, sm);
+  if (by_segments) reduce_by_segments<R, RED_COL_PARTS, uint16_t>(a.s, a.heads, blockIdx.z, blockIdx.y, blockIdx.x, sm);
+  else reduce_by_heads<R, uint16_t>(a.s, a.heads, blockIdx.y, blockIdx.x, sm);
 }
 
 }  // namespace mla
