@@ -45,7 +45,7 @@ struct SplitArgs {
   int batch, block_size, max_blocks, num_blocks, rank, nshards, layout;
   int G;          // split workgroups launched
   int min_tiles;  // fewest tiles a split workgroup is given
-  int seg_cost;   // tiles' worth of work charged for starting a request's segment
+  int seg_cost;   // tiles' worth of work charged per request for its segment boundaries (half before its tiles, half after)
   int q_len;      // query tokens per request: row set b is request b / q_len, token b % q_len
   float scale;    // softmax scale
   float c;        // softmax scale * log2(e)

@@ -50,9 +50,14 @@ __device__ __forceinline__ const int32_t* table_row(const SplitArgs& s, int b) {
 
 // Fills s_pref[0..batch] with the inclusive prefix sums of the requests' work
 // (s_pref[0] = 0) and returns the total T.  A request of n > 0 tiles weighs
-// n + seg_cost: the stream-K split then hands a workgroup that starts a
-// request (and pays its prologue: q, block-table window, pipeline fill) that
-// many fewer tiles.  Request b's tile k sits at position s_pref[b] + seg_cost + k.
+// n + seg_cost: a segment boundary inside a workgroup's range costs the end of
+// one segment (pipeline drain, partial write) and the start of the next
+// (block-table window, q, pipeline fill), so the request's positions carry
+// seg_head = seg_cost / 2 charge positions before its tiles and the rest after
+// them, and the stream-K split hands a workgroup whose range holds a boundary
+// that many fewer tiles.  Two workgroups that meet at a request boundary pay
+// one segment end and one segment start between them, so the halves keep
+// them balanced too.  Request b's tile k sits at position s_pref[b] + seg_head + k.
 // All threads of the block call it.
 template <int THREADS>
 __device__ int plan_tiles(const SplitArgs& s, int tile, int* s_pref, int* s_wsum) {
@@ -91,18 +96,22 @@ __device__ int plan_tiles(const SplitArgs& s, int tile, int* s_pref, int* s_wsum
   return uni(carry);
 }
 
+__device__ __forceinline__ int seg_head(const SplitArgs& s) { return s.seg_cost >> 1; }
+__device__ __forceinline__ int seg_tail(const SplitArgs& s) { return s.seg_cost - (s.seg_cost >> 1); }
+
 // Tiles [t0, t1) of request b (positions [pb, pe)) that fall in the workgroup's
-// positions [p0, p1); empty (t1 <= t0) when the range holds only the request's
-// charged start or nothing of it.
+// positions [p0, p1); empty (t1 <= t0) when the range holds only charge
+// positions of the request or nothing of it.
 struct SegTiles {
   int t0, t1, ntiles;
 };
 __device__ __forceinline__ SegTiles seg_tiles(const SplitArgs& s, int pb, int pe, int p0, int p1) {
-  const int r0 = pb + s.seg_cost;  // position of tile 0
+  const int r0 = pb + seg_head(s);  // position of tile 0
+  const int re = pe - seg_tail(s);  // position after the last tile
   SegTiles t;
   t.t0 = (p0 > r0 ? p0 : r0) - r0;
-  t.t1 = (p1 < pe ? p1 : pe) - r0;
-  t.ntiles = pe - r0;
+  t.t1 = (p1 < re ? p1 : re) - r0;
+  t.ntiles = re - r0;
   return t;
 }
 
@@ -125,7 +134,7 @@ __device__ __forceinline__ int find_request(const int* s_pref, int batch, int p)
 
 // ---------------------------------------------------------------- split reduce
 //
-// Request b's tiles [pb + seg_cost, pe) of the stream-K partition (T positions
+// Request b's tiles [pb + seg_head, pe - seg_tail) of the stream-K partition (T positions
 // over geff workgroups) were covered by workgroups g0..g1; workgroup g wrote the
 // un-normalized (m, l, o) of request b to slot g + b.  A request held by one
 // workgroup was finished by that workgroup and is skipped here; a request with
@@ -153,8 +162,8 @@ __device__ __forceinline__ SegRange seg_range(const SplitArgs& s, int b) {
   const int T = s.ws_meta[1 + s.batch];
   if (pe <= pb || geff <= 0 || T <= 0) return {0, 0};
   // workgroups holding the request's first and last tile
-  const int g0 = (int)(((int64_t)(pb + s.seg_cost + 1) * geff - 1) / T);
-  const int g1 = (int)(((int64_t)pe * geff - 1) / T);
+  const int g0 = (int)(((int64_t)(pb + seg_head(s) + 1) * geff - 1) / T);
+  const int g1 = (int)(((int64_t)(pe - seg_tail(s)) * geff - 1) / T);
   return {g0, g1 - g0 + 1};
 }
 

@@ -310,10 +310,15 @@ __device__ __forceinline__ void tie_q(QOps& q) {
 // bf16 block (rows of 1152 B, contiguous in HBM and in LDS), spread over the
 // waves.  A per-lane load of the MFMA operand layout touches 16 head rows per
 // instruction; the staged copy reads q in whole contiguous KiBs.
+// The copies are issued by waves QW0 .. NWAVE - 1 only, so waves below QW0 can
+// wait for loads of their own without waiting for q.
+constexpr int QW0 = 4;
 __device__ __forceinline__ void stage_q(const uint16_t* qreq, int heads, DCP_LDS char* qs) {
   const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave < QW0) return;
   const int nq = heads * (DK * 2) / 1024;  // exact: heads is a multiple of 16
-  for (int j = wave; j < nq; j += NWAVE) dma16((const char*)qreq + j * 1024 + lane * 16, qs + j * 1024);
+  for (int j = wave - QW0; j < nq; j += NWAVE - QW0)
+    dma16((const char*)qreq + j * 1024 + lane * 16, qs + j * 1024);
 }
 
 // This lane's q operands from the staged rows (the layouts of QOps).
@@ -561,27 +566,30 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
   pl.pg_hi = uni(min(s.max_blocks, (min(t1 * TILE, lr) - 1) / s.block_size + 1));
   pl.win.lo = pl.pg;
   pl.win.end = min(pl.pg_hi, pl.pg + TBL);
-  load_window(a, trow, sm, pl.pg, pl.pg_hi);
-  wait_vmcnt<0>();
-  wait_lgkm0();
-  barrier();
-  plan_prefetch(pl, sm);
 
-  // q goes to the last QST stages while the first A tiles' copies go out, so
-  // the two travel together; then q is read into registers, its stages are
-  // released and the remaining tiles of the ring are requested.
+  // q goes to the last QST stages (copies from waves QW0 and up) while waves
+  // below QW0 stage the block-table window, so the two latencies overlap;
+  // then the first A tiles are requested, q is read into registers once it
+  // has landed, its stages are released and the rest of the ring is requested.
   constexpr int QST = (64 * DK * 2 + STAGE - 1) / STAGE;  // stages holding up to 64 heads of q
   constexpr int A = NST - QST;                            // tiles requested before q is read
   static_assert(A >= 1 && A <= NST - 1, "q staging");
+  static_assert(TBL <= QW0 * 64, "the window is staged by the waves below QW0");
   DCP_LDS char* qs = tiles + A * STAGE;
   stage_q(a.q + (int64_t)b * heads * DK, heads, qs);
+  load_window(a, trow, sm, pl.pg, pl.pg_hi);
+  if (wave < QW0) wait_vmcnt<0>();  // the window's loads (these waves issued no q copies)
+  wait_lgkm0();
+  barrier();
+  plan_prefetch(pl, sm);
   // copy instructions this wave issues per tile: DMA_N, or one less where the
   // last round of slots does not reach this wave
   const bool full_round = uni(wave) + (DMA_N - 1) * NWAVE < CPT;
 #pragma unroll
   for (int j = 0; j < A; ++j)
     if (n > j) copy_all<FP8>(plan_next(a, trow, sm, pl, tiles + j * STAGE, true), goff, grow);
-  // the q copies are older than the tiles' copies issued since
+  // the q copies (waves QW0 and up) are older than the tiles' copies issued
+  // since; the other waves have only tile copies outstanding
   if (full_round) wait_tiles<A, DMA_N>(n);
   else wait_tiles<A, DMA_N - 1>(n);
   barrier();
@@ -679,15 +687,20 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(1024))) Smem<FP8> sm;
   const SplitArgs& s = a.s;
   const int tid = threadIdx.x;
-  const int g = blockIdx.x;
+  const int bid = blockIdx.x;
 
   const int T = plan_tiles<THREADS>(s, TILE, sm.pref, sm.wsum);
   const int geff = split_wgs(s, T);
-  if (g == 0) {
+  if (bid == 0) {
     for (int i = tid; i <= s.batch; i += THREADS) s.ws_meta[1 + i] = sm.pref[i];
     if (tid == 0) s.ws_meta[0] = geff;
   }
-  if (g >= geff) return;
+  if (bid >= geff) return;
+  // Workgroups go to the 8 XCDs round-robin (block i to XCD i mod 8).  The
+  // split ranges are numbered so that each XCD holds a contiguous run of
+  // them: neighbouring ranges, the pieces of one request, then share an L2
+  // for the request's q and block-table row.
+  const int g = uni(geff % 8 ? bid : (bid % 8) * (geff / 8) + bid / 8);
   const int p0 = uni((int)((int64_t)g * T / geff));
   const int p1 = uni((int)((int64_t)(g + 1) * T / geff));
 

@@ -59,9 +59,11 @@ def test_gqa_shapes(dev, hq, hkv, lens, n, layout, bs):
     check(W.Case(w, seed=1), dev)
 
 
-def test_gqa_zero_lengths_and_splits(dev, monkeypatch):
+@pytest.mark.parametrize("seg_cost", [0, 5])
+def test_gqa_zero_lengths_and_splits(dev, monkeypatch, seg_cost):
     monkeypatch.setenv("DCP_GQA_MIN_TILES", "1")
     monkeypatch.setenv("DCP_SPLIT_WGS", "37")
+    monkeypatch.setenv("DCP_GQA_SEG_COST", str(seg_cost))
     w = W.custom_workload(kind="gqa", batch=4, heads=64, kv_heads=8, seq_lens=(0, 5000, 17, 0), num_shards=2,
                           block_size=16, wid=301)
     check(W.Case(w, seed=2), dev)

@@ -85,11 +85,15 @@ def test_zero_length_requests(dev):
     check_case(W.Case(w, seed=2), dev)
 
 
-@pytest.mark.parametrize("min_tiles,wgs", [(1, 256), (3, 7), (8, 1), (2, 512), (1000, 256)])
-def test_split_plans(dev, monkeypatch, min_tiles, wgs):
-    """Same answer whatever the split of the tile list over workgroups."""
+@pytest.mark.parametrize("min_tiles,wgs,seg_cost", [(1, 256, 6), (3, 7, 1), (8, 1, 6), (2, 512, 0), (1000, 256, 6),
+                                                    (1, 64, 13), (1, 300, 5)])
+def test_split_plans(dev, monkeypatch, min_tiles, wgs, seg_cost):
+    """Same answer whatever the split of the tile list over workgroups,
+    including segment charges that put workgroup boundaries inside a
+    request's charge positions (odd and even charges split unevenly)."""
     monkeypatch.setenv("DCP_MLA_MIN_TILES", str(min_tiles))
     monkeypatch.setenv("DCP_SPLIT_WGS", str(wgs))
+    monkeypatch.setenv("DCP_MLA_SEG_COST", str(seg_cost))
     w = W.custom_workload(kind="mla", batch=5, heads=64, seq_lens=(3000, 1, 777, 5000, 64),
                           num_shards=2, wid=202)
     check_case(W.Case(w, seed=3), dev)

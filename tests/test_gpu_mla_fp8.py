@@ -35,10 +35,11 @@ def test_fp8_edge_lengths(dev, lens, n, layout, heads, bs, scale):
     check_case(W.Case(w, seed=1, kv_fp8_scale=scale), dev)
 
 
-@pytest.mark.parametrize("min_tiles,wgs", [(1, 256), (3, 7), (8, 1), (2, 512)])
-def test_fp8_split_plans(dev, monkeypatch, min_tiles, wgs):
+@pytest.mark.parametrize("min_tiles,wgs,seg_cost", [(1, 256, 6), (3, 7, 3), (8, 1, 6), (2, 512, 0), (1, 64, 11)])
+def test_fp8_split_plans(dev, monkeypatch, min_tiles, wgs, seg_cost):
     monkeypatch.setenv("DCP_MLA8_MIN_TILES", str(min_tiles))
     monkeypatch.setenv("DCP_SPLIT_WGS", str(wgs))
+    monkeypatch.setenv("DCP_MLA8_SEG_COST", str(seg_cost))
     w = W.custom_workload(kind="mla", batch=5, heads=64, seq_lens=(3000, 1, 777, 5000, 64),
                           num_shards=2, wid=401)
     check_case(W.Case(w, seed=3, kv_fp8_scale=W.FP8_SCALE), dev)
