@@ -163,7 +163,7 @@ dcp_status mla_partial(const dcp_mla_params* p, const void* q, const void* kv_ca
   a.s.q_len = qlen_of(p->q_len);
   a.s.G = env_int("DCP_SPLIT_WGS", cus < dcp::kMaxSplitWGs ? cus : dcp::kMaxSplitWGs, 1,
                   dcp::kMaxSplitWGs);
-  a.s.min_tiles = env_int(fp8 ? "DCP_MLA8_MIN_TILES" : "DCP_MLA_MIN_TILES", fp8 ? 8 : 4, 1, 1 << 20);
+  a.s.min_tiles = env_int(fp8 ? "DCP_MLA8_MIN_TILES" : "DCP_MLA_MIN_TILES", 4, 1, 1 << 20);
   a.s.seg_cost = env_int(fp8 ? "DCP_MLA8_SEG_COST" : "DCP_MLA_SEG_COST", 6, 0, 64);
   a.q = (const uint16_t*)q;
   a.kv = kv_cache;

@@ -696,11 +696,7 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
     if (tid == 0) s.ws_meta[0] = geff;
   }
   if (bid >= geff) return;
-  // Workgroups go to the 8 XCDs round-robin (block i to XCD i mod 8).  The
-  // split ranges are numbered so that each XCD holds a contiguous run of
-  // them: neighbouring ranges, the pieces of one request, then share an L2
-  // for the request's q and block-table row.
-  const int g = uni(geff % 8 ? bid : (bid % 8) * (geff / 8) + bid / 8);
+  const int g = bid;
   const int p0 = uni((int)((int64_t)g * T / geff));
   const int p1 = uni((int)((int64_t)(g + 1) * T / geff));
 

@@ -130,3 +130,24 @@ def test_long_segment_table_window(dev, monkeypatch, bs):
     w = W.custom_workload(kind="mla", batch=2, heads=64, seq_lens=(70001, 33), num_shards=2, block_size=bs,
                           wid=205)
     check_case(W.Case(w, seed=6), dev)
+
+
+def test_workspace_reuse_across_shapes(dev):
+    """One workspace (sized for the largest call) serves calls of different
+    batch sizes and split counts in a row, with the same results each time."""
+    big = W.custom_workload(kind="mla", batch=8, heads=64, seq_lens=(4000, 9000, 1, 300, 7000, 64, 2500, 10),
+                            num_shards=2, wid=207)
+    small = W.custom_workload(kind="mla", batch=1, heads=64, seq_lens=(30000,), num_shards=2, wid=208)
+    rb = ShardRun(W.Case(big, seed=8), 0, dev)
+    rs = ShardRun(W.Case(small, seed=9), 0, dev, workspace=rb.ws)
+    ref_b = [o.clone() for o in rb.run()]
+    ref_s = [o.clone() for o in rs.run()]
+    for _ in range(3):
+        ob, lb = rb.run(torch.empty_like(rb.out), torch.empty_like(rb.lse))
+        os_, ls = rs.run(torch.empty_like(rs.out), torch.empty_like(rs.lse))
+        torch.cuda.synchronize()
+        assert torch.equal(ob, ref_b[0]) and torch.equal(lb, ref_b[1])
+        assert torch.equal(os_, ref_s[0]) and torch.equal(ls, ref_s[1])
+    for b in range(big.batch):
+        o_ref, l_ref = oracle_rows(rb.case, b, list(range(64)), 0)
+        assert_rows_close(ref_b[0][b].cpu().numpy(), ref_b[1][b].cpu().numpy(), o_ref, l_ref, f"big b={b}")
