@@ -151,6 +151,7 @@ __device__ __forceinline__ int find_request(const int* s_pref, int batch, int p)
 //    lane) and add their sums in LDS.
 constexpr int REDUCE_THREADS = 512;
 constexpr int kReduceHeads = 8;  // heads per block in the by-heads mapping
+static_assert(kReduceHeads <= REDUCE_THREADS / 64, "one head per wave in the by-heads mapping");
 
 struct SegRange {
   int g0, nseg;  // first segment slot offset and segment count; nseg 0: empty request
@@ -190,6 +191,37 @@ __device__ __forceinline__ void seg_weights(const SplitArgs& s, int heads, int b
       s_M[j] = mx;
       s_L[j] = L;
     }
+  }
+  __syncthreads();
+}
+
+// Segment weights of one head h, the whole block working: thread t takes
+// segment t (nseg <= kMaxSplitWGs = REDUCE_THREADS), so every (m, l) pair is
+// read in one round trip.  Same results as seg_weights with nh = 1, into
+// s_w[i], s_M[0], s_L[0].
+static_assert(kMaxSplitWGs <= REDUCE_THREADS, "one segment per thread");
+__device__ __forceinline__ void seg_weights_one(const SplitArgs& s, int heads, int b, const SegRange& r, int h,
+                                                float* s_w, float* s_M, float* s_L, float (&red)[2][REDUCE_THREADS / 64]) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  float2 ml = make_float2(-__builtin_inff(), 0.f);
+  if (t < r.nseg) ml = *(const float2*)(s.ws_ml + ((size_t)(r.g0 + t + b) * heads + h) * 2);
+  const float wm = wave_max(ml.x);
+  if (lane == 0) red[0][wave] = wm;
+  __syncthreads();
+  float mx = red[0][0];
+#pragma unroll
+  for (int w = 1; w < REDUCE_THREADS / 64; ++w) mx = fmaxf(mx, red[0][w]);
+  const float wgt = t < r.nseg ? exp2_fast((ml.x - mx) * s.c) : 0.f;
+  if (t < r.nseg) s_w[t] = wgt;
+  const float ws = wave_sum(wgt * ml.y);
+  if (lane == 0) red[1][wave] = ws;
+  __syncthreads();
+  if (t == 0) {
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < REDUCE_THREADS / 64; ++w) L += red[1][w];
+    s_M[0] = mx;
+    s_L[0] = L;
   }
   __syncthreads();
 }
@@ -263,6 +295,7 @@ __device__ __forceinline__ void store_cols(float* p, const FVec<N>& r) {
 struct ReduceSmem {
   float w[kReduceHeads * kMaxSplitWGs];
   float M[kReduceHeads], L[kReduceHeads];
+  float red[2][REDUCE_THREADS / 64];  // per-wave maxima and sums of seg_weights_one
   float part[REDUCE_THREADS / 64][512];  // by-segments mapping: per-wave sums of a column part
 };
 
@@ -286,16 +319,26 @@ __device__ __forceinline__ void reduce_by_heads(const SplitArgs& s, int heads, i
     }
     return;
   }
-  seg_weights(s, heads, b, r, h0, nh, sm.w, sm.M, sm.L);
   const size_t stride = (size_t)heads * DV;
+  // the first two segments of this wave's head (a split request has at least
+  // two) are requested before the weights, so both round trips overlap; a wave
+  // past the group's heads reads a valid row it does not use
+  FVec<C> pre[2];
+  {
+    const int hp = min(h0 + wave, heads - 1);
+    const T* src = (const T*)s.ws_o + ((size_t)(r.g0 + b) * heads + hp) * DV + lane * C;
+    pre[0] = load_cols<C, T>(src);
+    pre[1] = load_cols<C, T>(src + stride);
+  }
+  seg_weights(s, heads, b, r, h0, nh, sm.w, sm.M, sm.L);
   for (int j = wave; j < nh; j += REDUCE_THREADS / 64) {
     const int h = h0 + j;
     const T* src = (const T*)s.ws_o + ((size_t)(r.g0 + b) * heads + h) * DV + lane * C;
     const float* w = sm.w + j * kMaxSplitWGs;
     FVec<C> acc;
 #pragma unroll
-    for (int k = 0; k < C; ++k) acc.v[k] = 0.f;
-    int i = 0;
+    for (int k = 0; k < C; ++k) acc.v[k] = w[0] * pre[0].v[k] + w[1] * pre[1].v[k];
+    int i = 2;
     for (; i + 4 <= r.nseg; i += 4) {
       FVec<C> x[4];
 #pragma unroll
@@ -338,15 +381,26 @@ __device__ __forceinline__ void reduce_by_segments(const SplitArgs& s, int heads
     }
     return;
   }
-  seg_weights(s, heads, b, r, h, 1, sm.w, sm.M, sm.L);
   const size_t stride = (size_t)heads * DV;
   const T* src = (const T*)s.ws_o + ((size_t)(r.g0 + b) * heads + h) * DV + col;
   constexpr int NW = REDUCE_THREADS / 64;
+  constexpr int U = 8;
+  // this wave's first U segments are requested before the weights (indices
+  // clamped into the request: loads past its last segment are not used)
+  FVec<C> pre[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) pre[u] = load_cols<C, T>(src + (size_t)min(wave + u * NW, r.nseg - 1) * stride);
+  seg_weights_one(s, heads, b, r, h, sm.w, sm.M, sm.L, sm.red);
   FVec<C> acc;
 #pragma unroll
   for (int k = 0; k < C; ++k) acc.v[k] = 0.f;
-  constexpr int U = 8;
-  int i = wave;
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (wave + u * NW < r.nseg) {
+#pragma unroll
+      for (int k = 0; k < C; ++k) acc.v[k] += sm.w[wave + u * NW] * pre[u].v[k];
+    }
+  int i = wave + U * NW;
   for (; i + (U - 1) * NW < r.nseg; i += U * NW) {
     FVec<C> x[U];
 #pragma unroll
