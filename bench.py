@@ -103,16 +103,36 @@ def vproj_bytes(w, q_len=1):
             + 2 * q_len * w.batch * w.heads * VPROJ_DVO * 2)
 
 
-def cpu_baseline(case, budget_s=10.0, q_len=1):
-    """The fp64 oracle on the host cores, on a bounded sample of the same step.
+def cpu_baseline(case, budget_s=10.0, q_len=1, budget_1core_s=5.0):
+    """The fp64 oracle on the host cores, on a bounded sample of the same step:
+    once with every BLAS thread (`value`, `cores`) and once on one thread
+    (`value_1core`), with the host CPU model.  See _oracle_step_us."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    us, sample = _oracle_step_us(case, budget_s, q_len)
+    threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    with threadpool_limits(limits=1):
+        us1, sample1 = _oracle_step_us(case, budget_1core_s, q_len)
+    return {"value": round(us, 1), "unit": "us/step", "cores": threads, "kind": "oracle", "sample": sample,
+            "value_1core": round(us1, 1), "sample_1core": sample1, "cpu": _cpu_model()}
 
-    The oracle computes the timed shards' partials request by request (its own
-    fp64 softmax attention over each shard slice, widened from the same bf16
-    inputs) and the LSE merge of the N partials; requests are taken in order,
-    cycling, until about `budget_s` seconds of oracle time are spent, and the
-    time is scaled by the fraction of the step's local tokens covered.  Input
-    widening is not timed.
-    """
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_step_us(case, budget_s, q_len):
+    """The oracle computes the timed shards' partials request by request (its
+    own fp64 softmax attention over each shard slice, widened from the same
+    bf16 inputs) and the LSE merge of the N partials; requests are taken in
+    order, cycling, until about `budget_s` seconds of oracle time are spent,
+    and the time is scaled by the fraction of the step's local tokens covered.
+    Input widening is not timed.  Returns (us per step, sample description)."""
     import oracle
     w = case.w
     ranks = list(w.ranks)
@@ -164,15 +184,9 @@ def cpu_baseline(case, budget_s=10.0, q_len=1):
         b = (b + 1) % w.batch
     frac = done_tokens / max(total_tokens, 1)
     us_per_step = t_spent / max(frac, 1e-12) * 1e6
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:  # pragma: no cover
-        cores = os.cpu_count()
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    return {"value": round(us_per_step, 1), "unit": "us/step", "cores": min(cores, threads), "kind": "oracle",
-            "sample": f"{reqs} request-steps ({q_len} query token(s) each) of the {w.batch}-request step "
-                      f"({frac:.2f} steps' worth of local "
-                      f"tokens), fp64 numpy, {t_spent:.1f} s of oracle time, scaled to one step"}
+    return us_per_step, (f"{reqs} request-steps ({q_len} query token(s) each) of the {w.batch}-request step "
+                         f"({frac:.2f} steps' worth of local tokens), fp64 numpy, {t_spent:.1f} s of oracle time, "
+                         f"scaled to one step")
 
 
 def main():
@@ -322,7 +336,9 @@ def main():
                 fn(i)
         return g
 
-    def timed_replay(g, reps=3):
+    replay_ms = {}
+
+    def timed_replay(g, reps=5, name=None):
         times = []
         for _ in range(reps):
             e0 = torch.cuda.Event(enable_timing=True)
@@ -333,6 +349,8 @@ def main():
                 e1.record(side)
             e1.synchronize()
             times.append(e0.elapsed_time(e1))
+        if name:
+            replay_ms[name] = sorted(times)
         return sorted(times)[len(times) // 2]  # median replay
 
     g_step = capture(step)
@@ -342,7 +360,7 @@ def main():
     with torch.cuda.stream(side):
         g_step.replay()  # warm the graph once
     torch.cuda.synchronize()
-    total_ms = timed_replay(g_step)
+    total_ms = timed_replay(g_step, name="step")
     ms_per_step = total_ms / args.steps
     part_ms = timed_replay(g_part)
     comb_ms = timed_replay(g_comb)
@@ -378,7 +396,8 @@ def main():
         "combine_us": round(comb_mean, 3),
         "epilogue": "dcp_combine_vproj_gate" if args.epilogue == "vproj" else "dcp_combine",
         "epilogue_gbps": round(alg_comb / (comb_mean * 1e-6) / 1e9, 1),
-        "timing": "K steps captured in one HIP graph; HIP events around each of 3 replays, median replay",
+        "timing": "K steps captured in one HIP graph; HIP events around each of 5 replays, median replay",
+        "step_us_replays": [round(t / args.steps * 1e3, 3) for t in replay_ms["step"]],
         "mfma_tflops": round(flops / (part_mean * 1e-6) / 1e12, 2),
         "mfma_frac": round(flops / (part_mean * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
         "roofline": {"bound": "hbm", "kernel": f"dcp_{w.kind}_decode_partial" + ("_fp8" if fp8 else ""),
