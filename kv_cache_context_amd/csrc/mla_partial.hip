@@ -696,7 +696,13 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
     if (tid == 0) s.ws_meta[0] = geff;
   }
   if (bid >= geff) return;
-  const int g = bid;
+  // Workgroups go to the 8 XCDs round-robin (block i to XCD i mod 8).  For
+  // multi-token steps the split ranges are numbered so that each XCD holds a
+  // contiguous run of them: the row sets of one request's tokens sit next to
+  // each other in the tile list and stream the same cache rows at about the
+  // same time, so neighbouring ranges on one XCD share its L2 (C4b at q_len 2:
+  // 4% faster; single-token steps gain nothing from it).
+  const int g = uni((s.q_len > 1 && geff % 8 == 0) ? (bid % 8) * (geff / 8) + bid / 8 : bid);
   const int p0 = uni((int)((int64_t)g * T / geff));
   const int p1 = uni((int)((int64_t)(g + 1) * T / geff));
 

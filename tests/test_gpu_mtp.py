@@ -74,6 +74,19 @@ CASES = [
 
 @pytest.mark.parametrize("kind,batch,heads,kvh,lens,block,n,layout,q_len", CASES)
 def test_mtp_partials_and_merge(dev, kind, batch, heads, kvh, lens, block, n, layout, q_len):
+    _check_mtp(dev, kind, batch, heads, kvh, lens, block, n, layout, q_len)
+
+
+@pytest.mark.parametrize("wgs", [64, 60])
+def test_mtp_xcd_grouped_ranges(dev, monkeypatch, wgs):
+    """Multi-token MLA steps whose split width is a multiple of 8 (64) number
+    their ranges per XCD; the same results as a split that is not (60)."""
+    monkeypatch.setenv("DCP_SPLIT_WGS", str(wgs))
+    monkeypatch.setenv("DCP_MLA_MIN_TILES", "1")
+    _check_mtp(dev, "mla", 3, 64, 1, (4000, 2500, 700), 64, 2, 0, 3)
+
+
+def _check_mtp(dev, kind, batch, heads, kvh, lens, block, n, layout, q_len):
     say(f"mtp {kind} b={batch} H={heads} lens={lens} B={block} N={n} layout={layout} q_len={q_len}")
     w = W.custom_workload(kind, batch=batch, heads=heads, kv_heads=kvh, seq_lens=lens, block_size=block,
                           num_shards=n, layout=layout, wid=300 + q_len)
