@@ -32,6 +32,16 @@ def _req(t: torch.Tensor, dtype, ndim: int, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _req_ws(ws: torch.Tensor, *tensors):
+    """The workspace: a contiguous device tensor on the same device as the
+    call's other tensors (its byte size is checked by the library)."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on a HIP device")
+    for t in tensors:
+        if t.device != ws.device:
+            raise ValueError(f"all tensors must be on one device ({t.device} vs {ws.device})")
+
+
 def mla_params(*, batch, num_heads, block_size, max_blocks_per_seq, num_blocks, shard_rank, num_shards,
                layout, max_seq_len_hint, softmax_scale, kv_lora_rank=512, rope_dim=64,
                q_len=1) -> _abi.dcp_mla_params:
@@ -89,6 +99,7 @@ def _mla_check(p, q, kv_cache, kv_dtypes, block_table, seq_lens, out, lse):
 
 def dcp_mla_decode_partial(p, q, kv_cache, block_table, seq_lens, out, lse, workspace, stream=None) -> None:
     _mla_check(p, q, kv_cache, (torch.bfloat16,), block_table, seq_lens, out, lse)
+    _req_ws(workspace, q, kv_cache, block_table, seq_lens, out, lse)
     _abi.check(_abi.dcp_mla_decode_partial(p, q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
                                            seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -100,6 +111,7 @@ def dcp_mla_decode_partial_fp8(p, q, kv_cache, kv_scale, block_table, seq_lens, 
     """MLA partial over an fp8 cache: kv_cache holds E4M3 codes (torch.float8_e4m3fn
     or uint8) [num_blocks, block_size, 576]; kv_scale dequantizes the whole cache."""
     _mla_check(p, q, kv_cache, (torch.float8_e4m3fn, torch.uint8), block_table, seq_lens, out, lse)
+    _req_ws(workspace, q, kv_cache, block_table, seq_lens, out, lse)
     _abi.check(_abi.dcp_mla_decode_partial_fp8(p, q.data_ptr(), kv_cache.data_ptr(), float(kv_scale),
                                                block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                                                lse.data_ptr(), workspace.data_ptr(),
@@ -125,6 +137,7 @@ def dcp_gqa_decode_partial(p, q, k_cache, v_cache, block_table, seq_lens, out, l
         raise ValueError("block_table / seq_lens shape")
     if tuple(out.shape) != (_rows(p), p.num_q_heads, p.head_dim) or tuple(lse.shape) != (_rows(p), p.num_q_heads):
         raise ValueError("out/lse shape")
+    _req_ws(workspace, q, k_cache, v_cache, block_table, seq_lens, out, lse)
     _abi.check(_abi.dcp_gqa_decode_partial(p, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                            block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
                                            lse.data_ptr(), workspace.data_ptr(),
