@@ -2,7 +2,9 @@
 
 Each function validates shapes, dtypes, devices and contiguity of torch
 tensors, fills the parameter struct and calls the library entry point of the
-same name on the given stream.  No arithmetic of the method happens here.
+same name on the given stream (default: the current stream of the tensors'
+device), with the tensors' device current.  No arithmetic of the method
+happens here.
 """
 from __future__ import annotations
 
@@ -11,12 +13,24 @@ import torch
 from . import dcp as _abi
 
 
-def _stream(stream) -> int:
+def _stream(stream, device: torch.device) -> int:
+    """The raw hipStream_t: the given stream, or the current stream of the
+    tensors' device."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, torch.cuda.Stream):
+        if stream.device != device:
+            raise ValueError(f"stream is on {stream.device}, tensors on {device}")
         return stream.cuda_stream
     return int(stream)
+
+
+def _one_device(*tensors) -> torch.device:
+    """The single device of the call's tensors (None entries are skipped)."""
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) != 1:
+        raise ValueError(f"all tensors must be on one device, got {sorted(str(d) for d in devs)}")
+    return devs.pop()
 
 
 def _req(t: torch.Tensor, dtype, ndim: int, name: str):
@@ -32,14 +46,13 @@ def _req(t: torch.Tensor, dtype, ndim: int, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _req_ws(ws: torch.Tensor, *tensors):
+def _req_ws(ws: torch.Tensor, *tensors) -> torch.device:
     """The workspace: a contiguous device tensor on the same device as the
-    call's other tensors (its byte size is checked by the library)."""
+    call's other tensors (its byte size is checked by the library).  Returns
+    that device."""
     if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on a HIP device")
-    for t in tensors:
-        if t.device != ws.device:
-            raise ValueError(f"all tensors must be on one device ({t.device} vs {ws.device})")
+    return _one_device(ws, *tensors)
 
 
 def mla_params(*, batch, num_heads, block_size, max_blocks_per_seq, num_blocks, shard_rank, num_shards,
@@ -99,11 +112,12 @@ def _mla_check(p, q, kv_cache, kv_dtypes, block_table, seq_lens, out, lse):
 
 def dcp_mla_decode_partial(p, q, kv_cache, block_table, seq_lens, out, lse, workspace, stream=None) -> None:
     _mla_check(p, q, kv_cache, (torch.bfloat16,), block_table, seq_lens, out, lse)
-    _req_ws(workspace, q, kv_cache, block_table, seq_lens, out, lse)
-    _abi.check(_abi.dcp_mla_decode_partial(p, q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
-                                           seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                           _stream(stream)), "dcp_mla_decode_partial")
+    dev = _req_ws(workspace, q, kv_cache, block_table, seq_lens, out, lse)
+    with torch.cuda.device(dev):
+        _abi.check(_abi.dcp_mla_decode_partial(p, q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
+                                               seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                               _stream(stream, dev)), "dcp_mla_decode_partial")
 
 
 def dcp_mla_decode_partial_fp8(p, q, kv_cache, kv_scale, block_table, seq_lens, out, lse, workspace,
@@ -111,12 +125,13 @@ def dcp_mla_decode_partial_fp8(p, q, kv_cache, kv_scale, block_table, seq_lens, 
     """MLA partial over an fp8 cache: kv_cache holds E4M3 codes (torch.float8_e4m3fn
     or uint8) [num_blocks, block_size, 576]; kv_scale dequantizes the whole cache."""
     _mla_check(p, q, kv_cache, (torch.float8_e4m3fn, torch.uint8), block_table, seq_lens, out, lse)
-    _req_ws(workspace, q, kv_cache, block_table, seq_lens, out, lse)
-    _abi.check(_abi.dcp_mla_decode_partial_fp8(p, q.data_ptr(), kv_cache.data_ptr(), float(kv_scale),
-                                               block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
-                                               lse.data_ptr(), workspace.data_ptr(),
-                                               workspace.numel() * workspace.element_size(), _stream(stream)),
-               "dcp_mla_decode_partial_fp8")
+    dev = _req_ws(workspace, q, kv_cache, block_table, seq_lens, out, lse)
+    with torch.cuda.device(dev):
+        _abi.check(_abi.dcp_mla_decode_partial_fp8(p, q.data_ptr(), kv_cache.data_ptr(), float(kv_scale),
+                                                   block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                                                   lse.data_ptr(), workspace.data_ptr(),
+                                                   workspace.numel() * workspace.element_size(),
+                                                   _stream(stream, dev)), "dcp_mla_decode_partial_fp8")
 
 
 def dcp_gqa_decode_partial(p, q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace,
@@ -137,12 +152,13 @@ def dcp_gqa_decode_partial(p, q, k_cache, v_cache, block_table, seq_lens, out, l
         raise ValueError("block_table / seq_lens shape")
     if tuple(out.shape) != (_rows(p), p.num_q_heads, p.head_dim) or tuple(lse.shape) != (_rows(p), p.num_q_heads):
         raise ValueError("out/lse shape")
-    _req_ws(workspace, q, k_cache, v_cache, block_table, seq_lens, out, lse)
-    _abi.check(_abi.dcp_gqa_decode_partial(p, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                           block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
-                                           lse.data_ptr(), workspace.data_ptr(),
-                                           workspace.numel() * workspace.element_size(), _stream(stream)),
-               "dcp_gqa_decode_partial")
+    dev = _req_ws(workspace, q, k_cache, v_cache, block_table, seq_lens, out, lse)
+    with torch.cuda.device(dev):
+        _abi.check(_abi.dcp_gqa_decode_partial(p, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                               block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                                               lse.data_ptr(), workspace.data_ptr(),
+                                               workspace.numel() * workspace.element_size(),
+                                               _stream(stream, dev)), "dcp_gqa_decode_partial")
 
 
 def dcp_combine(partial_out, partial_lse, out_bf16=None, out_f32=None, lse_out=None, stream=None) -> None:
@@ -163,9 +179,11 @@ def dcp_combine(partial_out, partial_lse, out_bf16=None, out_f32=None, lse_out=N
         _req(lse_out, torch.float32, 2, "lse_out")
         if tuple(lse_out.shape) != (b, h):
             raise ValueError("lse_out shape")
+    dev = _one_device(partial_out, partial_lse, out_bf16, out_f32, lse_out)
     ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
-    _abi.check(_abi.dcp_combine(n, b, h, dv, partial_out.data_ptr(), partial_lse.data_ptr(), ptr(out_bf16),
-                                ptr(out_f32), ptr(lse_out), _stream(stream)), "dcp_combine")
+    with torch.cuda.device(dev):
+        _abi.check(_abi.dcp_combine(n, b, h, dv, partial_out.data_ptr(), partial_lse.data_ptr(), ptr(out_bf16),
+                                    ptr(out_f32), ptr(lse_out), _stream(stream, dev)), "dcp_combine")
 
 
 def dcp_combine_vproj_gate(partial_out, partial_lse, w_uv_t, gate=None, out_bf16=None, out_f32=None,
@@ -196,7 +214,9 @@ def dcp_combine_vproj_gate(partial_out, partial_lse, w_uv_t, gate=None, out_bf16
         _req(lse_out, torch.float32, 2, "lse_out")
         if tuple(lse_out.shape) != (b, h):
             raise ValueError("lse_out shape")
+    dev = _one_device(partial_out, partial_lse, w_uv_t, gate, out_bf16, out_f32, lse_out)
     ptr = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
-    _abi.check(_abi.dcp_combine_vproj_gate(n, b, h, dv, dvo, partial_out.data_ptr(), partial_lse.data_ptr(),
-                                           w_uv_t.data_ptr(), ptr(gate), ptr(out_bf16), ptr(out_f32),
-                                           ptr(lse_out), _stream(stream)), "dcp_combine_vproj_gate")
+    with torch.cuda.device(dev):
+        _abi.check(_abi.dcp_combine_vproj_gate(n, b, h, dv, dvo, partial_out.data_ptr(), partial_lse.data_ptr(),
+                                               w_uv_t.data_ptr(), ptr(gate), ptr(out_bf16), ptr(out_f32),
+                                               ptr(lse_out), _stream(stream, dev)), "dcp_combine_vproj_gate")

@@ -154,3 +154,11 @@ def test_ops_reject_cpu_tensors():
     t = torch.zeros((1, 64, 576), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ops.dcp_mla_decode_partial(p, t, t, t, t, t, t, t)
+
+
+def test_ops_one_device():
+    import torch
+    a = torch.zeros(1)
+    assert ops._one_device(a, None, torch.ones(2)) == torch.device("cpu")
+    with pytest.raises(ValueError):
+        ops._one_device(a, torch.zeros(1, device="meta"))
