@@ -142,7 +142,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Number of a request's L global tokens that live on shard r of n.
 // Round-robin: positions r, r+n, ...; contiguous: [r*C, min(L,(r+1)*C)), C = ceil(L/n).
-__device__ __forceinline__ int local_len(int L, int n, int r, int layout) {
+__host__ __device__ __forceinline__ int local_len(int L, int n, int r, int layout) {
   if (L <= 0) return 0;
   const int64_t LL = L;
   if (layout == 0) return LL > r ? (int)((LL - r + n - 1) / n) : 0;

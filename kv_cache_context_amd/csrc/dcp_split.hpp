@@ -22,7 +22,7 @@ namespace dcp {
 // request's L global positions.  The shard's part of the cache is cut from the
 // full length L (for the contiguous layout, runs of ceil(L / N)); the result is
 // capped at what one table row can address.
-__device__ __forceinline__ int clamp_len(const SplitArgs& s, int L, int j) {
+__host__ __device__ __forceinline__ int clamp_len(const SplitArgs& s, int L, int j) {
   int lr;
   if (s.q_len <= 1 || s.layout == 0) {
     lr = local_len(s.q_len <= 1 ? L : L - s.q_len + 1 + j, s.nshards, s.rank, s.layout);
@@ -96,8 +96,8 @@ __device__ int plan_tiles(const SplitArgs& s, int tile, int* s_pref, int* s_wsum
   return uni(carry);
 }
 
-__device__ __forceinline__ int seg_head(const SplitArgs& s) { return s.seg_cost >> 1; }
-__device__ __forceinline__ int seg_tail(const SplitArgs& s) { return s.seg_cost - (s.seg_cost >> 1); }
+__host__ __device__ __forceinline__ int seg_head(const SplitArgs& s) { return s.seg_cost >> 1; }
+__host__ __device__ __forceinline__ int seg_tail(const SplitArgs& s) { return s.seg_cost - (s.seg_cost >> 1); }
 
 // Tiles [t0, t1) of request b (positions [pb, pe)) that fall in the workgroup's
 // positions [p0, p1); empty (t1 <= t0) when the range holds only charge
@@ -105,7 +105,7 @@ __device__ __forceinline__ int seg_tail(const SplitArgs& s) { return s.seg_cost 
 struct SegTiles {
   int t0, t1, ntiles;
 };
-__device__ __forceinline__ SegTiles seg_tiles(const SplitArgs& s, int pb, int pe, int p0, int p1) {
+__host__ __device__ __forceinline__ SegTiles seg_tiles(const SplitArgs& s, int pb, int pe, int p0, int p1) {
   const int r0 = pb + seg_head(s);  // position of tile 0
   const int re = pe - seg_tail(s);  // position after the last tile
   SegTiles t;
@@ -115,7 +115,7 @@ __device__ __forceinline__ SegTiles seg_tiles(const SplitArgs& s, int pb, int pe
   return t;
 }
 
-__device__ __forceinline__ int split_wgs(const SplitArgs& s, int T) {
+__host__ __device__ __forceinline__ int split_wgs(const SplitArgs& s, int T) {
   if (T <= 0) return 0;
   const int want = (T + s.min_tiles - 1) / s.min_tiles;
   return want < s.G ? want : s.G;
@@ -157,7 +157,7 @@ struct SegRange {
   int g0, nseg;  // first segment slot offset and segment count; nseg 0: empty request
 };
 
-__device__ __forceinline__ SegRange seg_range(const SplitArgs& s, int b) {
+__host__ __device__ __forceinline__ SegRange seg_range(const SplitArgs& s, int b) {
   const int geff = s.ws_meta[0];
   const int pb = s.ws_meta[1 + b], pe = s.ws_meta[2 + b];
   const int T = s.ws_meta[1 + s.batch];
