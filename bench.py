@@ -211,7 +211,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs one GPU only; the N shards are simulated on one device. "
+        print(json.dumps({"error": "one GPU only: the N shards are simulated as slices on one device. "
                                    "Run with --gpus 1."}))
         sys.exit(2)
 
