@@ -72,13 +72,21 @@ def algorithmic_bytes(case, r, q_len=1):
     return kv + q + out + meta, kv
 
 
+def _shard_positions_below(L, lim, n, r, layout):
+    """How many of shard r's positions (of a cache of length L split over n
+    shards, in the input layout) lie below `lim`."""
+    import workloads as W
+    pos = W.local_positions(L, n, r, layout)  # a range
+    return len(range(pos.start, max(pos.start, min(pos.stop, lim)), pos.step))
+
+
 def attended(case, r, q_len):
-    """(request, token) pairs' attended positions on shard r, summed."""
-    import oracle
+    """(request, token) pairs' attended positions on shard r, summed: token j of
+    a q_len-token step attends the positions below L - q_len + 1 + j."""
     w = case.w
     if q_len == 1:
         return int(case.local_lens(r).sum())
-    return sum(len(oracle.query_positions(int(L), q_len, j, w.num_shards, r, w.layout))
+    return sum(_shard_positions_below(int(L), int(L) - q_len + 1 + j, w.num_shards, r, w.layout)
                for L in case.seq_lens for j in range(q_len))
 
 
