@@ -35,6 +35,8 @@
  *   `stream` (0 = the null stream of the current device) and return.  There
  *   is no device-to-host read and no synchronization.  Inputs must stay valid
  *   and unmodified until the enqueued work completes.
+ * - A call sizes its launch for the current device (hipGetDevice): make the
+ *   device that holds the buffers current, and pass a stream of that device.
  * - Argument errors are detected on the host before anything is enqueued; the
  *   call then returns a non-zero status and launches nothing.  A failed launch
  *   returns DCP_ERR_HIP; dcp_last_hip_error() gives the hipError_t value.
