@@ -633,9 +633,13 @@ __device__ __attribute__((always_inline)) inline bool run_segment(
     return false;
   }
   if (!preset) {
+    // barrier() does not wait on memory counters: each LDS flag write must
+    // have completed (lgkmcnt 0) before the barrier that publishes it
     if (tid == 0) sm.flag = 0;
+    wait_lgkm0();
     barrier();
     if (__any(ovf) && lane == 0) sm.flag = 1;
+    wait_lgkm0();
     barrier();
     const bool redo = uni(sm.flag) != 0;
     barrier();  // also: every wave is done with the tiles before they are refilled

@@ -72,10 +72,26 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); return uint16 bits.
 
     Inputs here are finite normal draws, so NaN handling is not needed.
+    Rounding adds 0x7FFF plus the kept part's lowest bit to the float32 bits
+    and drops the low 16 bits.  Done in pieces of 2^20 values so the
+    temporaries stay in the host caches (large caches are generated in
+    chunks of tens of millions of values).
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    u = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
-    return (u >> np.uint32(16)).astype(np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    flat = x.reshape(-1).view(np.uint32)
+    out = np.empty(flat.shape, np.uint16)
+    step = 1 << 20
+    tmp = np.empty(min(step, flat.size), np.uint32)
+    for i in range(0, flat.size, step):
+        u = flat[i:i + step]
+        t = tmp[:u.size]
+        np.right_shift(u, np.uint32(16), out=t)
+        np.bitwise_and(t, np.uint32(1), out=t)
+        np.add(t, np.uint32(0x7FFF), out=t)
+        np.add(t, u, out=t)
+        np.right_shift(t, np.uint32(16), out=t)
+        out[i:i + u.size] = t
+    return out.reshape(x.shape)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -84,8 +100,20 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def normal_bf16(key, shape) -> np.ndarray:
+    """bf16 bits of float32 standard normal draws from the generator keyed
+    ``key``, in C order.  The draws are taken in consecutive pieces of the one
+    stream (the same values as a single call) so no full-size float32
+    temporary is needed."""
     rng = np.random.default_rng(list(key))
-    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+    out = np.empty(shape, np.uint16)
+    flat = out.reshape(-1)
+    step = 1 << 20
+    buf = np.empty(min(step, flat.size), np.float32)
+    for i in range(0, flat.size, step):
+        x = buf[:min(step, flat.size - i)]
+        rng.standard_normal(out=x, dtype=np.float32)
+        flat[i:i + x.size] = f32_to_bf16_bits(x)
+    return out
 
 
 # ---------------------------------------------------------------- fp8 (E4M3) codes
