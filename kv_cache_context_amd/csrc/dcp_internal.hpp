@@ -90,6 +90,7 @@ struct VprojArgs {
 };
 
 hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream);
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_gqa_partial(const GqaArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_combine_vproj(const VprojArgs& a, hipStream_t stream);

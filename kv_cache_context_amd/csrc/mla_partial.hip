@@ -267,16 +267,6 @@ __device__ __forceinline__ void zero_tail(DCP_LDS char* stage, int valid) {
 // MAXIMUM only the scores' running maximum (see compute_tile).
 enum { FULL = 0, MAXIMUM = 1 };
 
-// Eight E4M3 codes (two dwords, code k in byte k % 4 of dword k / 4) widened
-// to bf16, in order.  The conversion is exact.
-__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
-  const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-  const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-  const auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-  const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
 // Byte-transposing LDS read: inside each group of 16 lanes, lane i receives
 // byte (i % 8) of the 8 bytes loaded by lanes 2k + i / 8, k = 0..7.  With lanes
 // 2k and 2k + 1 of a group pointing at bytes 0..7 and 8..15 of row k's 16-byte
