@@ -61,14 +61,16 @@
 extern "C" {
 #endif
 
-#define DCP_ABI_VERSION 2
+#define DCP_ABI_VERSION 3
 
 typedef enum {
   DCP_OK = 0,
   DCP_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, rank out of range ... */
   DCP_ERR_UNSUPPORTED = 2,      /* valid but not implemented (dims, head counts, block size) */
   DCP_ERR_WORKSPACE = 3,        /* workspace missing or smaller than *_workspace_bytes() */
-  DCP_ERR_HIP = 4               /* a HIP call failed; see dcp_last_hip_error() */
+  DCP_ERR_HIP = 4,              /* a HIP call failed; see dcp_last_hip_error() */
+  DCP_ERR_SCRATCH = 5           /* the call needs more than the fixed device scratch of
+                                   dcp_mla_decode_partial_noalloc (DCP_NOALLOC_SCRATCH_BYTES) */
 } dcp_status;
 
 /* How a request's token positions are spread over the N shards
@@ -141,6 +143,29 @@ dcp_status dcp_mla_decode_partial(const dcp_mla_params* p, const void* q, const 
                                   const int32_t* block_table, const int32_t* seq_lens, float* out,
                                   float* lse, void* workspace, size_t workspace_bytes,
                                   hipStream_t stream);
+
+/* dcp_mla_decode_partial for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops that forbid hipMalloc): the
+ * same computation and kernels, with the split workspace taken from a fixed
+ * array in device memory that the library holds for the life of the process,
+ * one per GPU (DCP_NOALLOC_SCRATCH_BYTES = 32 MiB each).  The call itself
+ * allocates nothing; on its first use on a device it looks up that device's
+ * array address (hipGetSymbolAddress) with the device current.
+ *
+ * The scratch needed is 256-byte-aligned metadata, (m, l) pairs and bf16
+ * split partials for (split workgroups + batch * q_len) slots of num_heads
+ * rows of 512, where the split uses one workgroup per compute unit: at 64
+ * heads and 256 compute units, batch * q_len up to 244 fits.  A larger call
+ * returns DCP_ERR_SCRATCH and launches nothing.
+ *
+ * Every call on a GPU shares that GPU's array (the scratch needs no
+ * clearing; the kernels write what they read).  Calls that overlap on one
+ * GPU race: order them on one stream.  Arguments, results and every other
+ * error are those of dcp_mla_decode_partial. */
+#define DCP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+dcp_status dcp_mla_decode_partial_noalloc(const dcp_mla_params* p, const void* q, const void* kv_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens, float* out,
+                                          float* lse, hipStream_t stream);
 
 /* dcp_mla_decode_partial over an fp8 latent cache.  The Kimi K3 optimizations
  * page ("Kimi K3 Performance Optimizations in vLLM", decode context

@@ -5,9 +5,17 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "dcp.h"
 #include "dcp_internal.hpp"
+
+// Split workspace of the no-allocation entry point: one array per GPU, held
+// for the life of the process.  Host code never uses the name `scratch` as an
+// address (on the host it is only a stand-in for the device symbol): the
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current (scratch_addr below).
+static __device__ __align__(256) char scratch[DCP_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -132,10 +140,33 @@ dcp_status gqa_check(const dcp_gqa_params* p) {
   return DCP_OK;
 }
 
+std::mutex g_scratch_mu;
+void* g_scratch_addr[64];
+
+// The current device's scratch address (looked up on first use).
+hipError_t scratch_addr(void** addr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = a;
+  }
+  *addr = g_scratch_addr[dev];
+  return hipSuccess;
+}
+
 // Both MLA entry points: bf16 cache, or E4M3 cache with dequantization scale kv_scale.
+// noalloc: the workspace arguments are ignored and the split workspace is the
+// device scratch, laid out for this call's split width.
 dcp_status mla_partial(const dcp_mla_params* p, const void* q, const void* kv_cache, bool fp8, float kv_scale,
                        const int32_t* block_table, const int32_t* seq_lens, float* out, float* lse,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                       void* workspace, size_t workspace_bytes, hipStream_t stream, bool noalloc = false) {
   dcp_status st = mla_check(p);
   if (st != DCP_OK) return st;
   if (fp8) {
@@ -150,19 +181,29 @@ dcp_status mla_partial(const dcp_mla_params* p, const void* q, const void* kv_ca
       !aligned(seq_lens, 4) || !aligned(lse, 4))
     return DCP_ERR_INVALID_ARGUMENT;
   const int rows = rows_of(p->batch, p->q_len);
-  const dcp::WsLayout wl = dcp::ws_layout(rows, p->num_heads, 512, 2);
-  if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
+  dcp::WsLayout wl;
+  if (!noalloc) {
+    wl = dcp::ws_layout(rows, p->num_heads, 512, 2);
+    if (!workspace || workspace_bytes < wl.total || !aligned(workspace, 256)) return DCP_ERR_WORKSPACE;
+  }
   hipError_t herr = hipSuccess;
   const int cus = device_cus(&herr);
   if (cus <= 0) return hip_status(herr);
+  const int G = env_int("DCP_SPLIT_WGS", cus < dcp::kMaxSplitWGs ? cus : dcp::kMaxSplitWGs, 1, dcp::kMaxSplitWGs);
+  if (noalloc) {
+    // slots g + b of a split over G workgroups: G + rows of them
+    wl = dcp::ws_layout_slots((size_t)G + (size_t)rows, p->num_heads, 512, 2);
+    if (wl.total > DCP_NOALLOC_SCRATCH_BYTES) return DCP_ERR_SCRATCH;
+    herr = scratch_addr(&workspace);
+    if (herr != hipSuccess) return hip_status(herr);
+  }
 
   dcp::MlaArgs a;
   a.s = split_args(rows, p->block_size, p->max_blocks_per_seq, p->num_blocks, p->shard_rank,
                    p->num_shards, p->layout, fp8 ? p->softmax_scale * kv_scale : p->softmax_scale, block_table,
                    seq_lens, out, lse, workspace, wl);
   a.s.q_len = qlen_of(p->q_len);
-  a.s.G = env_int("DCP_SPLIT_WGS", cus < dcp::kMaxSplitWGs ? cus : dcp::kMaxSplitWGs, 1,
-                  dcp::kMaxSplitWGs);
+  a.s.G = G;
   a.s.min_tiles = env_int(fp8 ? "DCP_MLA8_MIN_TILES" : "DCP_MLA_MIN_TILES", 4, 1, 1 << 20);
   a.s.seg_cost = env_int(fp8 ? "DCP_MLA8_SEG_COST" : "DCP_MLA_SEG_COST", 6, 0, 64);
   a.q = (const uint16_t*)q;
@@ -190,6 +231,7 @@ const char* dcp_status_string(dcp_status s) {
     case DCP_ERR_UNSUPPORTED: return "unsupported configuration";
     case DCP_ERR_WORKSPACE: return "workspace missing or too small";
     case DCP_ERR_HIP: return "HIP error";
+    case DCP_ERR_SCRATCH: return "call needs more than the fixed device scratch of the no-allocation entry point";
   }
   return "unknown status";
 }
@@ -213,6 +255,12 @@ dcp_status dcp_mla_decode_partial_fp8(const dcp_mla_params* p, const void* q, co
                                       hipStream_t stream) {
   return mla_partial(p, q, kv_cache, true, kv_scale, block_table, seq_lens, out, lse, workspace, workspace_bytes,
                      stream);
+}
+
+dcp_status dcp_mla_decode_partial_noalloc(const dcp_mla_params* p, const void* q, const void* kv_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens, float* out,
+                                          float* lse, hipStream_t stream) {
+  return mla_partial(p, q, kv_cache, false, 1.0f, block_table, seq_lens, out, lse, nullptr, 0, stream, true);
 }
 
 size_t dcp_gqa_workspace_bytes(const dcp_gqa_params* p) {

@@ -24,14 +24,18 @@ struct WsLayout {
   size_t meta_off, ml_off, o_off, total;
 };
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline WsLayout ws_layout(int batch, int heads, int dv, size_t o_bytes) {
+// Layout for `slots` partial slots (a call whose split uses G workgroups
+// needs G + batch slots; ws_layout reserves the most any call uses).
+inline WsLayout ws_layout_slots(size_t slots, int heads, int dv, size_t o_bytes) {
   WsLayout w;
-  const size_t slots = (size_t)kMaxSplitWGs + (size_t)batch;
   w.meta_off = 0;
   w.ml_off = align256(sizeof(int32_t) * (kMaxBatch + 2));
   w.o_off = w.ml_off + align256(sizeof(float) * slots * heads * 2);
   w.total = w.o_off + align256(o_bytes * slots * heads * dv);
   return w;
+}
+inline WsLayout ws_layout(int batch, int heads, int dv, size_t o_bytes) {
+  return ws_layout_slots((size_t)kMaxSplitWGs + (size_t)batch, heads, dv, o_bytes);
 }
 
 struct SplitArgs {

@@ -24,12 +24,15 @@ DCP_ERR_INVALID_ARGUMENT = 1
 DCP_ERR_UNSUPPORTED = 2
 DCP_ERR_WORKSPACE = 3
 DCP_ERR_HIP = 4
+DCP_ERR_SCRATCH = 5
+DCP_NOALLOC_SCRATCH_BYTES = 32 << 20
 DCP_LAYOUT_ROUND_ROBIN = 0
 DCP_LAYOUT_CONTIGUOUS = 1
 
 # every symbol the header declares
 EXPORTED = (
     "dcp_mla_workspace_bytes", "dcp_mla_decode_partial", "dcp_mla_decode_partial_fp8",
+    "dcp_mla_decode_partial_noalloc",
     "dcp_gqa_workspace_bytes", "dcp_gqa_decode_partial",
     "dcp_combine", "dcp_combine_vproj_gate", "dcp_status_string", "dcp_last_hip_error", "dcp_abi_version",
 )
@@ -89,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.dcp_mla_decode_partial_fp8.argtypes = [ctypes.POINTER(dcp_mla_params), _P, _P, ctypes.c_float, _P, _P, _P,
                                              _P, _P, ctypes.c_size_t, _P]
     L.dcp_mla_decode_partial_fp8.restype = ctypes.c_int
+    L.dcp_mla_decode_partial_noalloc.argtypes = [ctypes.POINTER(dcp_mla_params), _P, _P, _P, _P, _P, _P, _P]
+    L.dcp_mla_decode_partial_noalloc.restype = ctypes.c_int
     L.dcp_gqa_workspace_bytes.argtypes = [ctypes.POINTER(dcp_gqa_params)]
     L.dcp_gqa_workspace_bytes.restype = ctypes.c_size_t
     L.dcp_gqa_decode_partial.argtypes = [ctypes.POINTER(dcp_gqa_params), _P, _P, _P, _P, _P, _P, _P, _P,
@@ -144,6 +149,12 @@ def dcp_mla_decode_partial_fp8(p: dcp_mla_params, q: int, kv_cache: int, kv_scal
                                stream: int) -> int:
     return int(lib().dcp_mla_decode_partial_fp8(ctypes.byref(p), q, kv_cache, kv_scale, block_table, seq_lens,
                                                 out, lse, workspace, workspace_bytes, stream))
+
+
+def dcp_mla_decode_partial_noalloc(p: dcp_mla_params, q: int, kv_cache: int, block_table: int, seq_lens: int,
+                                   out: int, lse: int, stream: int) -> int:
+    return int(lib().dcp_mla_decode_partial_noalloc(ctypes.byref(p), q, kv_cache, block_table, seq_lens, out, lse,
+                                                    stream))
 
 
 def dcp_gqa_decode_partial(p: dcp_gqa_params, q: int, k_cache: int, v_cache: int, block_table: int,

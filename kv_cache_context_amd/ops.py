@@ -120,6 +120,17 @@ def dcp_mla_decode_partial(p, q, kv_cache, block_table, seq_lens, out, lse, work
                                                _stream(stream, dev)), "dcp_mla_decode_partial")
 
 
+def dcp_mla_decode_partial_noalloc(p, q, kv_cache, block_table, seq_lens, out, lse, stream=None) -> None:
+    """dcp_mla_decode_partial with the library's fixed device scratch as the
+    split workspace (nothing is allocated)."""
+    _mla_check(p, q, kv_cache, (torch.bfloat16,), block_table, seq_lens, out, lse)
+    dev = _one_device(q, kv_cache, block_table, seq_lens, out, lse)
+    with torch.cuda.device(dev):
+        _abi.check(_abi.dcp_mla_decode_partial_noalloc(p, q.data_ptr(), kv_cache.data_ptr(), block_table.data_ptr(),
+                                                       seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                                       _stream(stream, dev)), "dcp_mla_decode_partial_noalloc")
+
+
 def dcp_mla_decode_partial_fp8(p, q, kv_cache, kv_scale, block_table, seq_lens, out, lse, workspace,
                                stream=None) -> None:
     """MLA partial over an fp8 cache: kv_cache holds E4M3 codes (torch.float8_e4m3fn

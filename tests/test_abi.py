@@ -23,7 +23,7 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == set(dcp.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
-    assert dcp.dcp_abi_version() == 2
+    assert dcp.dcp_abi_version() == 3
 
 
 def test_struct_layout_matches_header():
@@ -43,6 +43,7 @@ def test_workspace_grows_with_query_tokens():
 def test_status_strings():
     assert dcp.status_string(0) == "ok"
     assert "workspace" in dcp.status_string(3)
+    assert "scratch" in dcp.status_string(5)
     assert dcp.status_string(99) == "unknown status"
 
 
@@ -92,6 +93,17 @@ def test_mla_pointer_and_workspace_checks():
     # workspace grows with batch and heads only
     assert dcp.dcp_mla_workspace_bytes(mla(batch=4)) > need
     assert dcp.dcp_mla_workspace_bytes(mla(max_seq_len_hint=100)) == need
+
+
+def test_mla_noalloc_validation():
+    """The no-allocation entry point validates like dcp_mla_decode_partial
+    before it looks at the device (no GPU here: a valid call would need one)."""
+    f = dcp.dcp_mla_decode_partial_noalloc
+    assert f(mla(num_shards=0), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == 1
+    assert f(mla(num_heads=17), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == 2
+    assert f(mla(), 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0) == 1
+    assert f(mla(), FAKE, FAKE + 2, FAKE, FAKE, FAKE, FAKE, 0) == 1
+    assert f(mla(batch=0), 0, 0, 0, 0, 0, 0, 0) == 0
 
 
 def test_mla_fp8_validation():
