@@ -11,7 +11,8 @@ The default workload is c4, the long-context configuration: one step is the
 1M-token request with all 8 shards processed (8 partial calls + the combine,
 part c4a) followed by the 128-request batch at 64K context on shard 1 of 8
 (one partial call + the combine, part c4b).  Each single configuration
-(c0 .. c4b) can be selected with --workload.
+(c0 .. c4b, and c3kv1: the GQA example with one KV head per rank) can be
+selected with --workload.
 
 Cold cache: before every timed graph replay an untimed pass reads and writes
 a buffer of twice the 256 MB Infinity Cache, so nothing a replay reads is

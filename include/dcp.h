@@ -195,7 +195,7 @@ dcp_status dcp_mla_decode_partial_fp8(const dcp_mla_params* p, const void* q, co
 typedef struct {
   int32_t batch;              /* >= 0                                                       */
   int32_t num_q_heads;        /* Hq                                                         */
-  int32_t num_kv_heads;       /* Hkv: a multiple of 4; Hq a multiple of Hkv, Hq/Hkv <= 16   */
+  int32_t num_kv_heads;       /* Hkv: 1..64; Hq a multiple of Hkv, Hq/Hkv <= 64            */
   int32_t head_dim;           /* D; must be 128                                             */
   int32_t block_size;         /* tokens per cache block; a multiple of 16, 16..1024         */
   int32_t max_blocks_per_seq;

@@ -135,8 +135,8 @@ dcp_status gqa_check(const dcp_gqa_params* p) {
                               p->max_seq_len_hint, p->softmax_scale);
   if (st != DCP_OK) return st;
   if (p->head_dim != 128) return DCP_ERR_UNSUPPORTED;
-  if (p->num_kv_heads % 4 != 0 || p->num_kv_heads > 64) return DCP_ERR_UNSUPPORTED;
-  if (p->num_q_heads / p->num_kv_heads > 16) return DCP_ERR_UNSUPPORTED;
+  if (p->num_kv_heads > 64) return DCP_ERR_UNSUPPORTED;
+  if (p->num_q_heads / p->num_kv_heads > 64) return DCP_ERR_UNSUPPORTED;
   return DCP_OK;
 }
 
@@ -292,8 +292,9 @@ dcp_status dcp_gqa_decode_partial(const dcp_gqa_params* p, const void* q, const 
                    p->num_shards, p->layout, p->softmax_scale, block_table, seq_lens, out, lse,
                    workspace, wl);
   a.s.q_len = qlen_of(p->q_len);
-  // one workgroup column per group of 4 KV heads; together they fill the chip once
-  const int groups = p->num_kv_heads / 4;
+  // one workgroup column per group of KV heads streamed together; together
+  // they fill the chip once
+  const int groups = p->num_kv_heads / dcp::gqa_heads_per_workgroup(p->num_kv_heads);
   int g = (cus + groups - 1) / groups;
   if (g > dcp::kMaxSplitWGs) g = dcp::kMaxSplitWGs;
   a.s.G = env_int("DCP_SPLIT_WGS", g, 1, dcp::kMaxSplitWGs);

@@ -84,19 +84,46 @@ def oracle_rows(case: W.Case, b: int, heads, r: int | None):
     """Oracle (o, lse) for request b, the given heads, over shard r's slice
     (r=None: the whole sequence)."""
     w = case.w
-    q = oracle.widen_bf16(case.q[b, heads])
     L = int(case.seq_lens[b])
     if r is None:
         pos = np.arange(L)
     else:
         pos = oracle.shard_positions(L, w.num_shards, r, w.layout)
+    rows = case.rows_at(b, pos) if len(pos) else None
+    return oracle_on_rows(case, b, heads, rows)
+
+
+def oracle_all_shards(case: W.Case, b: int, heads):
+    """Oracle (o, lse) of every shard's slice of request b, from one pass over
+    the request's stored rows, and (last) the oracle's merge of them, which
+    equals unsharded attention (pinned by the merge invariant); the merge avoids
+    widening a whole 1M-token request at once."""
+    w = case.w
+    L = int(case.seq_lens[b])
+    logical = case.kv_logical(b)
+    if w.kind == "mla":
+        logical = [logical]
+    res = []
+    for r in range(w.num_shards):
+        pos = oracle.shard_positions(L, w.num_shards, r, w.layout)
+        say(f"    oracle b={b} shard {r}: {len(pos)} positions")
+        res.append(oracle_on_rows(case, b, heads, [x[pos] for x in logical] if len(pos) else None))
+    res.append(oracle.merge(np.stack([p[0] for p in res]), np.stack([p[1] for p in res])))
+    return res
+
+
+def oracle_on_rows(case: W.Case, b: int, heads, rows):
+    """Oracle (o, lse) for request b and the given heads over the stored rows
+    ``rows`` (as ``Case.rows_at`` returns them; None: no tokens)."""
+    w = case.w
+    q = oracle.widen_bf16(case.q[b, heads])
     if w.kind == "mla" and case.kv_fp8_scale is not None:
-        bits = case.rows_at(b, pos)[0] if len(pos) else np.zeros((0, w.dk), np.uint8)
+        bits = rows[0] if rows is not None else np.zeros((0, w.dk), np.uint8)
         return oracle.mla_attention_fp8(q, bits, case.kv_fp8_scale, w.scale, w.kv_lora_rank)
     if w.kind == "mla":
-        kv = oracle.widen_bf16(case.rows_at(b, pos)[0]) if len(pos) else np.zeros((0, w.dk))
+        kv = oracle.widen_bf16(rows[0]) if rows is not None else np.zeros((0, w.dk))
         return oracle.mla_attention(q, kv, w.scale, w.kv_lora_rank)
-    k, v = case.rows_at(b, pos) if len(pos) else (np.zeros((0, w.kv_heads, w.head_dim), np.uint16),) * 2
+    k, v = rows if rows is not None else (np.zeros((0, w.kv_heads, w.head_dim), np.uint16),) * 2
     k = oracle.widen_bf16(k)
     v = oracle.widen_bf16(v)
     hq = w.heads

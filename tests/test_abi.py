@@ -122,7 +122,8 @@ def test_mla_fp8_validation():
 
 @pytest.mark.parametrize("kw,status", [
     (dict(num_q_heads=60), 1), (dict(num_kv_heads=0), 1), (dict(shard_rank=4), 1), (dict(batch=-3), 1),
-    (dict(head_dim=64), 2), (dict(num_kv_heads=2, num_q_heads=16), 2), (dict(num_q_heads=256, num_kv_heads=8), 2),
+    (dict(head_dim=64), 2), (dict(num_q_heads=128, num_kv_heads=1), 2), (dict(num_q_heads=128, num_kv_heads=128), 2),
+    (dict(num_q_heads=1024, num_kv_heads=8), 2),
     (dict(block_size=24), 2), (dict(max_seq_len_hint=4 * 64 * 16 + 1), 1),
 ])
 def test_gqa_validation(kw, status):

@@ -112,8 +112,8 @@ def test_fp8_multi_token(dev):
 
 
 @pytest.mark.parametrize("name,reqs,heads", [
-    ("c4b", [0, 64, 127], [0, 31, 63]),
-    ("c2", [0, 11, 31], [0, 40, 63]),
+    ("c4b", [0, 64, 127], [0, 21, 42, 63]),
+    ("c2", [0, 11, 31], [0, 17, 40, 63]),
 ])
 def test_fp8_full_size_sampled(dev, name, reqs, heads):
     """The fp8 cache at the benchmark workloads' full sizes (timed shard only;

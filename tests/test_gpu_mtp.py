@@ -69,6 +69,8 @@ CASES = [
     ("gqa", 1, 32, 4, (513,), 32, 2, 1, 16),
     ("mla", 2, 16, 1, (3, 50), 16, 2, 1, 5),       # L < q_len, contiguous
     ("gqa", 2, 16, 4, (2, 40), 16, 4, 0, 4),       # L < q_len, round-robin
+    ("gqa", 2, 8, 1, (700, 19), 16, 2, 0, 3),      # one KV head per rank
+    ("gqa", 2, 16, 2, (333, 64), 32, 2, 1, 4),     # two KV heads per rank, contiguous
 ]
 
 

@@ -36,6 +36,7 @@ def _run(dev, n, b, h, dv, dvo, empty, gated=True, seed=0):
 
 @pytest.mark.parametrize("n,b,h,dv,dvo,empty", [
     (8, 128, 64, 512, 128, 0.1),   # batch-128 step shape: 8 shards, 64 heads
+    (8, 32, 64, 512, 128, 0.05),   # batch-32 ragged step shape
     (8, 1, 64, 512, 128, 0.0),     # one request: a 16-row block with 15 rows past the batch
     (4, 19, 5, 64, 48, 0.3),       # ragged batch over two row blocks, odd head count
     (1, 3, 16, 512, 128, 0.0),     # one shard: the merge is the identity

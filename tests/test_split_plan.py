@@ -44,6 +44,8 @@ def test_workload_shapes():
     check([65536] * 128, nshards=8, rank=1)                            # batch 128
     check([1 << 20], nshards=8, rank=7)                                # 1M tokens, last shard
     check([131072] * 16, nshards=4, rank=1, block_size=16, G=128, min_tiles=16, seg_cost=0, tile=16)  # GQA
+    check([131072] * 16, nshards=2, rank=1, block_size=16, G=256, min_tiles=16, seg_cost=0, tile=64)  # GQA, 1 KV head
+    check([70000, 3, 17, 64], nshards=2, rank=0, block_size=16, G=128, min_tiles=1, seg_cost=0, tile=32)  # 2 KV heads
 
 
 def test_degenerate_plans():
@@ -74,4 +76,4 @@ def test_random_plans(seed):
         nshards = int(rng.choice([1, 2, 3, 4, 8, 16]))
         check(lens, q_len=q_len, nshards=nshards, rank=int(rng.integers(0, nshards)), layout=int(rng.integers(0, 2)),
               block_size=int(rng.choice([16, 32, 48, 64, 128])), G=int(rng.integers(1, 513)),
-              min_tiles=int(rng.integers(1, 17)), seg_cost=int(rng.integers(0, 14)), tile=int(rng.choice([16, 32])))
+              min_tiles=int(rng.integers(1, 17)), seg_cost=int(rng.integers(0, 14)), tile=int(rng.choice([16, 32, 64])))

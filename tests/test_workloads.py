@@ -91,6 +91,9 @@ def test_workload_shapes():
     assert c3.max_blocks_per_seq() == 2048 and c3.local_lens(1)[0] == 32768
     c4b = W.Case(w["c4b"])
     assert c4b.local_lens(1).sum() == 128 * 8192
+    kv1 = W.Case(w["c3kv1"])
+    assert (w["c3kv1"].heads, w["c3kv1"].kv_heads, w["c3kv1"].num_shards) == (8, 1, 2)
+    assert kv1.local_lens(1)[0] == 65536 and kv1.max_blocks_per_seq() == 4096
 
 
 def test_e4m3_encoder_matches_torch():
@@ -133,3 +136,17 @@ def test_fp8_case_quantizes_the_bf16_draws():
     for j, t in enumerate(pos):
         blk = sc.block_table[0, j // 16]
         assert np.array_equal(sc.pools[0][blk, j % 16], l8[t])
+
+
+def test_e4m3_fast_encoder_equals_grid_search():
+    """The bit-level encoder gives the codes of the nearest-value search over
+    the code table on every code, every midpoint and its neighbours, clamped
+    magnitudes and random draws at the workloads' scale."""
+    grid = W._E4M3.astype(np.float32)
+    mids = ((grid[1:].astype(np.float64) + grid[:-1]) / 2).astype(np.float32)
+    edge = np.concatenate([grid, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+                           np.array([0.0, 448, 449, 464, 479.9, 480, 1e30, 2.0 ** -6, 2.0 ** -10, 1e-45], np.float32)])
+    rng = np.random.default_rng(11)
+    for x in (edge, -edge, rng.standard_normal(1 << 21, dtype=np.float32) / np.float32(W.FP8_SCALE),
+              rng.standard_normal(1 << 20, dtype=np.float32) * np.float32(0.01)):
+        assert np.array_equal(W.f32_to_e4m3_bits(x), W.f32_to_e4m3_bits_grid(x))

@@ -132,9 +132,11 @@ _E4M3 = _e4m3_grid()
 FP8_SCALE = 6.0 / 448.0
 
 
-def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+def f32_to_e4m3_bits_grid(x: np.ndarray) -> np.ndarray:
     """Round values to the nearest E4M3 code (ties to the even code), clamping
-    magnitudes to 448; returns uint8 codes.  Inputs are finite."""
+    magnitudes to 448; returns uint8 codes.  Inputs are finite.  Reference form:
+    a search over the table of code values (slow; ``f32_to_e4m3_bits`` gives the
+    same codes)."""
     x = np.asarray(x, dtype=np.float32)
     a = np.minimum(np.abs(x), np.float32(448.0))
     grid = _E4M3.astype(np.float32)  # exact: every E4M3 value is a float32 value
@@ -143,6 +145,34 @@ def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
     up = (a - lo > hi - a) | ((a - lo == hi - a) & (i % 2 == 0))
     code = np.where(up, i, i - 1).astype(np.uint8)
     return np.where(np.signbit(x), code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def _e4m3_codes(a: np.ndarray) -> np.ndarray:
+    """E4M3 codes of magnitudes 0 <= a <= 448 (float32), nearest, ties to even."""
+    # normal range (a >= 2^-6): round the float32 significand to 3 bits, ties to
+    # even, on the bit pattern (a carry out of the significand bumps the exponent)
+    bits = a.view(np.uint32)
+    r = (bits + np.uint32(0x7FFFF) + ((bits >> np.uint32(20)) & np.uint32(1))) >> np.uint32(20)
+    # r = (biased float32 exponent << 3) | 3-bit significand; E4M3 bias is 7, float32's 127
+    normal = (r - np.uint32((127 - 7) << 3)).astype(np.int64)
+    # below 2^-6 the codes are multiples of 2^-9 (code 8 is 2^-6 itself)
+    sub = np.rint(a * np.float32(512.0)).astype(np.int64)
+    return np.where(a < np.float32(2.0 ** -6), sub, normal).astype(np.uint8)
+
+
+def f32_to_e4m3_bits(x: np.ndarray) -> np.ndarray:
+    """Round values to the nearest E4M3 code (ties to the even code), clamping
+    magnitudes to 448; returns uint8 codes.  Inputs are finite."""
+    x = np.asarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    flat_x, flat_o = x.reshape(-1), out.reshape(-1)
+    step = 1 << 20
+    for i in range(0, flat_x.size, step):
+        xs = flat_x[i:i + step]
+        a = np.minimum(np.abs(xs), np.float32(448.0))
+        code = _e4m3_codes(a)
+        flat_o[i:i + step] = np.where(np.signbit(xs), code | np.uint8(0x80), code)
+    return out
 
 
 # ---------------------------------------------------------------- layouts
@@ -242,6 +272,12 @@ WORKLOADS = {
     "c4b": Workload("c4b", 5, "mla", batch=128, heads=64, block_size=64, num_shards=8, ranks=(1,),
                     seq_lens=(65536,) * 128, scale=MLA_SCALE,
                     description="MLA b=128, H=64, L=64K, shard 1 of 8 (8K local), B=64, combine over 8"),
+    # the DCP post's GQA deployment example (4 KV heads, tp 8, dcp 2): each rank
+    # holds 8 query heads and one KV head; C3's lengths and block size
+    "c3kv1": Workload("c3kv1", 6, "gqa", batch=16, heads=8, kv_heads=1, head_dim=128, block_size=16,
+                      num_shards=2, ranks=(1,), seq_lens=(131072,) * 16, scale=GQA_SCALE,
+                      description="GQA b=16, 8 q / 1 KV head per rank, D=128, L=128K, shard 1 of 2, B=16, "
+                                  "combine over 2"),
 }
 
 
