@@ -211,8 +211,6 @@ dcp_status mla_partial(const dcp_mla_params* p, const void* q, const void* kv_ca
   a.heads = p->num_heads;
   a.fp8 = fp8;
   a.vscale = fp8 ? kv_scale : 1.0f;
-  // the latent-split kernel is in development and off by default
-  if (env_int("DCP_MLA_KSPLIT", 0, 0, 1)) return hip_status(dcp::launch_mla_decode(a, stream));
   return hip_status(dcp::launch_mla_partial(a, stream));
 }
 

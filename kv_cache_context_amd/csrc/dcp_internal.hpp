@@ -94,7 +94,6 @@ struct VprojArgs {
 };
 
 hipError_t launch_mla_partial(const MlaArgs& a, hipStream_t stream);
-hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_gqa_partial(const GqaArgs& a, hipStream_t stream);
 // KV heads one GQA workgroup streams together (4, 2 or 1: the largest dividing Hkv).
 int gqa_heads_per_workgroup(int hkv);

@@ -724,9 +724,11 @@ __global__ __launch_bounds__(THREADS, 1) void partial_kernel(MlaArgs a) {
 }
 
 #ifndef DCP_MLA_RED_COL_PARTS
-#define DCP_MLA_RED_COL_PARTS 2
+#define DCP_MLA_RED_COL_PARTS 4
 #endif
-constexpr int RED_COL_PARTS = DCP_MLA_RED_COL_PARTS;  // column parts of the by-segments reduce
+// column parts of the by-segments reduce: 4 gives 256 blocks for 64 heads (one
+// per CU), measured ~0.5 us faster per call than 2 at 64 and 256 segments
+constexpr int RED_COL_PARTS = DCP_MLA_RED_COL_PARTS;
 
 __global__ __launch_bounds__(REDUCE_THREADS) void reduce_kernel(MlaArgs a, int by_segments) {
   __shared__ ReduceSmem sm;
