@@ -94,9 +94,14 @@ def report(prof: str, wl: str, kind: str, bench_args: str | None = None) -> tupl
     """bench_args: the bench arguments of the runs (default --workload <wl>); the kernel-trace run adds
     --no-cpu-baseline except for c1, the counter runs their own short-run flags."""
     base = bench_args if bench_args is not None else f"--workload {wl}"
-    kt_args = base + ("" if base == "--workload c1" else " --no-cpu-baseline")
+    # the default workload's trace is of the default command itself (CPU
+    # baseline leg included); c1 keeps its CPU baseline too
+    if base == "--workload c4":
+        kt_args = ""
+    else:
+        kt_args = base + ("" if base == "--workload c1" else " --no-cpu-baseline")
     kt_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {prof}/{wl} -o kt -- "
-              f"python -u bench.py {kt_args}")
+              f"python -u bench.py {kt_args}").rstrip()
     pmc_cmd = (f"rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d {prof}/{wl}_<counter> -o p -- "
                f"python -u bench.py {base} --steps 5 --warmup 1 --no-cpu-baseline --calibration-copy")
     bench = None
@@ -114,7 +119,12 @@ def report(prof: str, wl: str, kind: str, bench_args: str | None = None) -> tupl
     if bench:
         keep = {k: bench[k] for k in ("value", "unit", "partial_us", "combine_us", "step_hbm_gbps", "mfma_tflops")}
         keep["roofline"] = {k: bench["roofline"][k] for k in ("achieved", "peak", "frac", "bytes_per_launch")}
-        keep["config"] = {k: bench["config"][k] for k in ("workload", "q_len") if k in bench["config"]}
+        keep["config"] = {k: bench["config"][k] for k in ("workload", "q_len", "kv_dtype") if k in bench["config"]}
+        if "parts" in bench and len(bench["parts"]) > 1:
+            keep["parts"] = [{k: p[k] for k in ("workload", "partial_launches", "partial_us", "partial_frac")}
+                             for p in bench["parts"]]
+        if "cpu_baseline" in bench:
+            keep["cpu_baseline"] = bench["cpu_baseline"]
         keep["epilogue"] = bench.get("epilogue")
         lines += ["bench line of the traced run (HIP-event timing of graph replays; `partial_us` is one",
                   "partial call = partial_kernel + reduce_kernel).  Kernel tracing adds a few us to every",
