@@ -24,6 +24,11 @@ CASES = {
                    dict(q_scale_pow2=3, needles=[(0, 2500, 5), (1, 8999, 0)])),
     "gqa": (dict(kind="gqa", batch=3, heads=64, kv_heads=8, head_dim=128, seq_lens=(20000, 700, 0),
                  block_size=16, num_shards=4, wid=604), {}),
+    # one and two KV heads per workgroup: sub-tile waves merged through LDS
+    "gqa_kv1": (dict(kind="gqa", batch=3, heads=8, kv_heads=1, head_dim=128, seq_lens=(20000, 700, 5),
+                     block_size=16, num_shards=2, wid=605), {}),
+    "gqa_kv2": (dict(kind="gqa", batch=2, heads=32, kv_heads=2, head_dim=128, seq_lens=(9000, 33),
+                     block_size=32, num_shards=2, wid=606), {}),
 }
 
 
