@@ -29,35 +29,19 @@
 #include "dcp_device.hpp"
 #include "dcp_internal.hpp"
 #include "dcp_split.hpp"
+#include "gqa_layout.hpp"
 
 namespace dcp {
 namespace gqa {
 
-constexpr int D = 128;                 // head dim
-constexpr int HROW = D * 2;            // bytes per (token, head) row
-constexpr int HALF = 16 * 1024;        // the K (or V) part of a stage
+// (head dim, part size, copy slots and the operand offsets: gqa_layout.hpp)
 constexpr int STAGE = 2 * HALF;        // K then V
 constexpr int NST = 4;
 constexpr int THREADS = 256;
-constexpr int NWAVE = THREADS / 64;
-constexpr int CPI = 4;                 // 1 KiB copy instructions per wave per part (16 per part)
-constexpr int DMA_N = 2 * CPI;         // per wave per tile (8)
+constexpr int DMA_N = 2 * CPI;         // copies per wave per tile (8)
 constexpr int KS = D / 32;             // score k-steps (4)
 constexpr int VB = D / 16;             // value column blocks (8)
 constexpr int TBL = 1024;
-
-// Tile geometry for HG KV heads per workgroup.
-template <int HG>
-struct Geo {
-  static_assert(HG == 1 || HG == 2 || HG == 4, "KV heads per workgroup");
-  static constexpr int SUB = 4 / HG;           // 16-token sub-tiles per tile (one per wave of a head)
-  static constexpr int TROW = HG * HROW;       // bytes per token in a tile
-  static constexpr int TILE = 16 * SUB;        // tokens per tile
-  static_assert(TILE * TROW == HALF, "a part is 16 KiB");
-};
-
-// Chunk swizzle of token row t inside one head's 16 chunks of 16 bytes.
-__host__ __device__ constexpr int swz(int t) { return t & 15; }
 
 // Segment-end exchange of the waves of one KV head (SUB > 1): per (head,
 // sub-tile >= 1, query block) slot, the output block and each column's
@@ -137,21 +121,13 @@ __device__ __forceinline__ TileCopy plan_copy(const GqaArgs& a, const int32_t* t
   return t;
 }
 
-// Copy slot of this wave's j-th copy of a part: 1 KiB holding SUB tokens x HG
-// heads.  With one sub-tile (HG = 4) the waves interleave tokens; otherwise
-// wave w takes four consecutive slots, all inside its sub-tile w / HG.
-template <int HG>
-__device__ __forceinline__ int copy_slot(int wave, int j) {
-  return Geo<HG>::SUB == 1 ? 4 * j + wave : 4 * wave + j;
-}
-
 // Copy i of a tile for this wave: i < CPI -> K, else V.
 template <int HG>
 __device__ __forceinline__ void copy_part(const TileCopy& t, int i, const uint32_t (&voff)[CPI]) {
   if (!t.valid) return;
   const int wave = uni(threadIdx.x >> 6);
   const int j = i % CPI;
-  DCP_LDS char* dst = t.stage + (i < CPI ? 0 : HALF) + copy_slot<HG>(wave, j) * 1024;
+  DCP_LDS char* dst = t.stage + (i < CPI ? 0 : HALF) + copy_dst_offset<HG>(wave, j, 0);
   dma16_sbase(i < CPI ? t.kbase : t.vbase, voff[j], dst);
 }
 
@@ -182,11 +158,9 @@ __device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int sub, in
   const int lane = threadIdx.x & 63;
   const int g4 = lane >> 4, r16 = lane & 15;
   // ---- scores S^T[tok][head col]: A = K row (token r16 of the sub-tile), B = q^T
-  const DCP_LDS char* kp = st + (16 * sub + r16) * G::TROW + hk * HROW;
-  const int fz = swz(r16);
   bf16x8 kf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const DCP_LDS bf16x8*)(kp + (((4 * ks + g4) ^ fz) * 16));
+  for (int ks = 0; ks < KS; ++ks) kf[ks] = *(const DCP_LDS bf16x8*)(st + k_read_offset<HG>(sub, r16, hk, 4 * ks + g4));
   copy_part<HG>(nxt, 0, voff);
   copy_part<HG>(nxt, 1, voff);
   f32x4 sc[NQB];
@@ -233,14 +207,9 @@ __device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int sub, in
   copy_part<HG>(nxt, 5, voff);
 
   // ---- values O^T[col][head] += V^T[col][tok] . P^T[tok][head]
-  const int row = 4 * g4 + (r16 >> 2);  // token of the sub-tile this lane addresses
-  const int fv = swz(row);
-  const int hb = (r16 & 3) >> 1;
-  const int byte = (r16 & 1) * 8;
-  const DCP_LDS char* vp = st + HALF + (16 * sub + row) * G::TROW + hk * HROW + byte;
   i16x4 vt[VB];
 #pragma unroll
-  for (int cb = 0; cb < VB; ++cb) vt[cb] = lds_read_tr16(vp + (((2 * cb + hb) ^ fv) * 16));
+  for (int cb = 0; cb < VB; ++cb) vt[cb] = lds_read_tr16(st + HALF + v_read_offset<HG>(sub, g4, r16, hk, cb));
   copy_part<HG>(nxt, 6, voff);
   copy_part<HG>(nxt, 7, voff);
 #pragma unroll
@@ -265,17 +234,10 @@ __device__ __forceinline__ void run_segment(const GqaArgs& a, Smem& sm, int grou
   const int lr = uni(clamped_local_len(s, b));
   const int32_t* trow = table_row(s, b);
 
-  // lane offsets of the copies from the wave's sub-tile base: copy slot c holds
-  // tile tokens c*SUB .. +SUB-1, lane l the 16-byte chunk (l % 16) of head
-  // (l / 16) % HG of token c*SUB + l / (16 HG), chunk index swizzled per token
+  // lane offsets of the copies from the wave's sub-tile base
   uint32_t voff[CPI];
 #pragma unroll
-  for (int j = 0; j < CPI; ++j) {
-    const int tok = copy_slot<HG>(wave, j) * G::SUB + lane / (16 * HG);  // token of the tile
-    const int h = (lane >> 4) % HG, ch = lane & 15;
-    const int rel = tok - 16 * (wave / HG);                               // from the copy sub-tile's token 0
-    voff[j] = (uint32_t)(rel * a.hkv * HROW + h * HROW + ((ch ^ swz(tok)) * 16));
-  }
+  for (int j = 0; j < CPI; ++j) voff[j] = copy_src_offset<HG>(wave, j, lane, a.hkv);
 
   bf16x8 qf[NQB][KS];
 #pragma unroll
