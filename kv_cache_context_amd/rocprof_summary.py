@@ -36,7 +36,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {
     "mla": ["csrc/mla_partial.hip", "csrc/dcp_device.hpp", "csrc/dcp_split.hpp", "csrc/dcp_internal.hpp", "build.py"],
     "mla8": ["csrc/mla_partial.hip", "csrc/dcp_device.hpp", "csrc/dcp_split.hpp", "csrc/dcp_internal.hpp", "build.py"],
-    "gqa": ["csrc/gqa_partial.hip", "csrc/dcp_device.hpp", "csrc/dcp_split.hpp", "csrc/dcp_internal.hpp", "build.py"],
+    "gqa": ["csrc/gqa_partial.hip", "csrc/gqa_layout.hpp", "csrc/dcp_device.hpp", "csrc/dcp_split.hpp",
+            "csrc/dcp_internal.hpp", "build.py"],
     "combine": ["csrc/combine.hip", "csrc/dcp_device.hpp", "csrc/dcp_internal.hpp", "build.py"],
 }
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
