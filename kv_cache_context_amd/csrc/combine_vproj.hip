@@ -31,7 +31,6 @@ constexpr int ROWS = 16;      // requests per workgroup (one MFMA row block)
 constexpr int THREADS = 256;  // 4 waves
 constexpr int MAXN = 64;      // shards
 constexpr int MAXDV = 1024;
-constexpr int MAXNB = 16;     // output column blocks of 16 (Dvo <= 256)
 
 // NQ: column blocks per wave (1, 2 or 4); grid (row blocks, heads, column
 // groups): workgroup z takes column blocks [z * nbw, (z + 1) * nbw).

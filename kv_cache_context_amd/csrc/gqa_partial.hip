@@ -154,7 +154,6 @@ __device__ __forceinline__ void compute_tile(const DCP_LDS char* st, int sub, in
                                              const bf16x8 (&qf)[NQB][KS], f32x4 (&acc)[NQB][VB],
                                              float (&m)[NQB], float (&l)[NQB], float c, const TileCopy& nxt,
                                              const uint32_t (&voff)[CPI]) {
-  using G = Geo<HG>;
   const int lane = threadIdx.x & 63;
   const int g4 = lane >> 4, r16 = lane & 15;
   // ---- scores S^T[tok][head col]: A = K row (token r16 of the sub-tile), B = q^T
